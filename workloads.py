@@ -1,0 +1,131 @@
+"""Seeded synthetic inputs shared by the tests, bench.py and the oracle checks.
+
+This module holds only workload shapes and random-number recipes; it contains
+none of linear attention's arithmetic, so both the HIP path and the oracle can
+take their inputs from it without sharing any method code.
+
+Every tensor is drawn on the CPU with ``torch.Generator("cpu")`` (deterministic
+across machines), in float32 from N(0, 1), optionally multiplied by a power of
+two (0.125 = 1/sqrt(64), exact in every float format), and rounded to the
+workload's element type with round-to-nearest-even.  Draw order is Q, K, V.
+
+The named workloads follow the shapes on the pages: CIFAR-10 autoregressive
+generation is 32*32*3 = 3072 steps per image ("Transformers Are RNNs: Linear
+Attention" knowledge note, "Why This Exists"); the running model has
+d_model 512, h 8, d_k = d_v = 64 and scales to n = 128K tokens ("Why Replace
+Attention?", "The Running Example").  No dataset is read: values are i.i.d.
+Gaussian stand-ins for activations.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, Tuple
+
+import torch
+
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@dataclass(frozen=True)
+class ForwardWorkload:
+    name: str
+    causal: bool
+    dtype: str
+    B: int
+    H: int
+    N: int
+    C: int = 64
+    M: int = 64
+    scale: float = 1.0
+    seed: int = 0
+    note: str = ""
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.N
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    dtype: str
+    sequences: int
+    H: int
+    steps: int
+    C: int = 64
+    M: int = 64
+    scale: float = 1.0
+    seed: int = 0
+    note: str = ""
+
+    @property
+    def heads(self) -> int:
+        return self.sequences * self.H
+
+
+WORKLOADS: Dict[str, object] = {
+    "causal_f32_b1h1n256": ForwardWorkload(
+        "causal_f32_b1h1n256", True, "f32", 1, 1, 256, seed=1001,
+        note="small causal case the fp64 oracle finishes in well under a second"),
+    "noncausal_bf16_b8h8n4096": ForwardWorkload(
+        "noncausal_bf16_b8h8n4096", False, "bf16", 8, 8, 4096, scale=0.125, seed=1002,
+        note="non-causal, bf16 storage, fp32 accumulation"),
+    "causal_bf16_b16h8n3072": ForwardWorkload(
+        "causal_bf16_b16h8n3072", True, "bf16", 16, 8, 3072, seed=1003,
+        note="shaped like autoregressive 32x32x3 image generation, d_model 512"),
+    "causal_bf16_b2h8n131072": ForwardWorkload(
+        "causal_bf16_b2h8n131072", True, "bf16", 2, 8, 131072, scale=0.125, seed=1004,
+        note="long-context causal forward, fp32 state"),
+    "decode_f32_s256h8_3072steps": DecodeWorkload(
+        "decode_f32_s256h8_3072steps", "f32", 256, 8, 3072, seed=1005,
+        note="256 concurrent sequences x 8 heads, 3072 sequential steps"),
+}
+
+
+def draw_qkv(B: int, H: int, N: int, C: int, M: int, dtype: str, seed: int,
+             scale: float = 1.0) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Q [B,H,N,C], K [B,H,N,C], V [B,H,N,M] on the CPU, drawn in that order."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    out = []
+    for last in (C, C, M):
+        x = torch.randn((B, H, N, last), dtype=torch.float32, generator=g)
+        if scale != 1.0:
+            x.mul_(scale)
+        out.append(x.to(DTYPES[dtype]).contiguous())
+    return out[0], out[1], out[2]
+
+
+def forward_inputs(w: ForwardWorkload):
+    return draw_qkv(w.B, w.H, w.N, w.C, w.M, w.dtype, w.seed, w.scale)
+
+
+def decode_step_seed(w: DecodeWorkload, t: int) -> int:
+    return w.seed * 1_000_000 + int(t)
+
+
+def draw_decode_step(heads: int, C: int, M: int, dtype: str, seed: int,
+                     scale: float = 1.0) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """q [heads,C], k [heads,C], v [heads,M] for one decode step."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    out = []
+    for last in (C, C, M):
+        x = torch.randn((heads, last), dtype=torch.float32, generator=g)
+        if scale != 1.0:
+            x.mul_(scale)
+        out.append(x.to(DTYPES[dtype]).contiguous())
+    return out[0], out[1], out[2]
+
+
+def decode_inputs(w: DecodeWorkload, t: int):
+    return draw_decode_step(w.heads, w.C, w.M, w.dtype, decode_step_seed(w, t), w.scale)
+
+
+def to_oracle_array(t: torch.Tensor):
+    """CPU tensor -> numpy array in a form the oracle reads (bf16 as raw uint16 bits)."""
+    import numpy as np
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype in (torch.float32, torch.float64):
+        return t.numpy()
+    raise TypeError(f"unsupported dtype {t.dtype}")
