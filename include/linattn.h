@@ -1,0 +1,170 @@
+/*
+ * linattn.h -- C ABI of liblinattn.so: linear attention with the elu(x)+1
+ * feature map on AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("Why Replace Attention? The Softmax Bottleneck and the Path
+ * to Linear Time", §5.3, §6.2, §7.1, §7.2; "Transformers Are RNNs: Linear
+ * Attention" knowledge note, "Reassociate the Products" and "Turn Causal
+ * Attention into a Recurrence"):
+ *
+ *   phi(x) = elu(x) + 1  (x + 1 for x > 0, e^x otherwise), applied elementwise
+ *   S_i = sum_{j in J(i)} phi(k_j) v_j^T   (C x M),   z_i = sum_{j in J(i)} phi(k_j)
+ *   o_i = phi(q_i)^T S_i / phi(q_i)^T z_i
+ *
+ * with J(i) = {0..i} (causal, inclusive) or {0..N-1} (non-causal).  There is
+ * no epsilon in the denominator: phi > 0, so every denominator is positive
+ * for finite inputs.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are device pointers (hipMalloc / PyTorch CUDA tensors) unless a
+ *     comment says otherwise; all must be 16-byte aligned.
+ *   - Tensors are contiguous row-major.  Q, K: [B, H, N, C]; V, O: [B, H, N, M].
+ *   - This version supports C = M = 64 only (other values: LINATTN_ERR_SHAPE).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *     asynchronous: they validate on the host, enqueue kernels on `stream` and
+ *     return.  Device faults surface at the caller's next synchronisation.
+ *   - Validation happens on the host before anything is enqueued; a call that
+ *     returns an error has written no device memory.
+ *   - The library allocates no device memory and keeps none between calls.
+ *     Scratch space is the caller's `workspace`.
+ *   - The library is reentrant.  Its only global state is a per-thread error
+ *     message, a per-device attribute cache and the optional kernel timer.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LINATTN_OK = 0,
+    LINATTN_ERR_NULL = 1,      /* a required pointer is NULL */
+    LINATTN_ERR_SHAPE = 2,     /* negative size, C or M != 64, or a size that overflows */
+    LINATTN_ERR_DTYPE = 3,     /* unknown element type */
+    LINATTN_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned */
+    LINATTN_ERR_ALIAS = 5,     /* an output overlaps an input */
+    LINATTN_ERR_WORKSPACE = 6, /* workspace too small (or NULL while bytes are needed) */
+    LINATTN_ERR_HIP = 7,       /* the HIP runtime reported an error at launch */
+    LINATTN_ERR_ARG = 8        /* any other invalid argument */
+} linattn_status;
+
+typedef enum {
+    LINATTN_F32 = 0,  /* IEEE binary32 */
+    LINATTN_BF16 = 1  /* bfloat16; arithmetic is fp32 throughout */
+} linattn_dtype;
+
+/* Version of this interface (major * 10000 + minor * 100 + patch). */
+int linattn_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *linattn_status_string(linattn_status s);
+
+/* Message describing the last error returned on the calling thread (static
+ * per-thread buffer, never NULL; empty after a successful call). */
+const char *linattn_last_error(void);
+
+/* Bytes of device workspace `linattn_forward` needs for these arguments on the
+ * current device (0 when the chosen plan needs none).  Returns 0 for invalid
+ * arguments; `linattn_forward` reports those. */
+size_t linattn_forward_workspace_bytes(int B, int H, int N, int C, int M, linattn_dtype dt, int causal);
+
+/*
+ * linattn_forward -- the chunked parallel forward over whole sequences.
+ *
+ *   causal != 0: o_i uses tokens j <= i ("Why Replace Attention?", §7.1; the
+ *   causal prefix sums of §7.2 carried across chunks).
+ *   causal == 0: o_i uses every token ("Why Replace Attention?", §6.2).
+ *
+ * Q, K: [B,H,N,C] in `dt`; V: [B,H,N,M] in `dt`; O: [B,H,N,M] in `dt`, written.
+ * Accumulation is fp32; bf16 outputs are rounded to nearest-even.
+ * workspace: device buffer of at least linattn_forward_workspace_bytes(...)
+ *   bytes (may be NULL when that is 0).  Its contents on entry do not matter.
+ * B == 0, H == 0 or N == 0: returns LINATTN_OK and enqueues nothing.
+ * Errors: NULL (Q, K, V, O), SHAPE, DTYPE, ALIGN, ALIAS (O overlaps Q, K or
+ *   V), WORKSPACE, HIP.
+ * Results are deterministic: the same inputs, sizes and device give
+ * bit-identical outputs.
+ */
+linattn_status linattn_forward(const void *Q, const void *K, const void *V, void *O, int B, int H, int N,
+                               int C, int M, linattn_dtype dt, int causal, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
+ * linattn_forward_state -- causal forward that starts from a given state and
+ * returns the state after the last token: the prefill side of the handoff to
+ * linattn_decode_step ("Transformers Are RNNs: Linear Attention" knowledge
+ * note, "Putting It Together": only S_i and Z_i are carried forward; "[Paper
+ * Review] Transformers are RNNs", §3.6: parallel in training, recurrent at
+ * inference).
+ *
+ * S0: [B*H, C, M] fp32 and z0: [B*H, C] fp32, the state before token 0; both
+ *   NULL means zero (S_0 = 0, z_0 = 0, "Why Replace Attention?", §7.2).  Both
+ *   or neither must be given.
+ * S_out: [B*H, C, M] fp32 and z_out: [B*H, C] fp32 receive S_N and z_N; both
+ *   NULL skips the write.  Both or neither must be given.  They may be the
+ *   same buffers as S0 / z0 (updated in place); they must not overlap Q, K,
+ *   V or O.
+ * Other arguments as linattn_forward with causal = 1.  With N == 0 the state
+ *   is copied through (S_out = S0 or 0).
+ */
+linattn_status linattn_forward_state(const void *Q, const void *K, const void *V, void *O, int B, int H,
+                                     int N, int C, int M, linattn_dtype dt, const float *S0, const float *z0,
+                                     float *S_out, float *z_out, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
+/* Workspace for linattn_forward_state (the causal plan plus state staging). */
+size_t linattn_forward_state_workspace_bytes(int B, int H, int N, int C, int M, linattn_dtype dt);
+
+/*
+ * linattn_decode_step -- one constant-state recurrent step for BH independent
+ * heads ("Why Replace Attention?", §7.2, steps 1-4; §7.4 constant work per
+ * step):
+ *   S += phi(k) v^T;  z += phi(k);  o = phi(q)^T S / phi(q)^T z   (read after update)
+ *
+ * S: [BH, C, M] fp32, S[h][c][m], read and updated in place.
+ * z: [BH, C] fp32, read and updated in place.
+ * q, k: [BH, C] in `dt`; v: [BH, M] in `dt`.  o: [BH, M] fp32, written.
+ * A fresh sequence starts from S = 0, z = 0 (caller clears them).
+ * BH == 0: LINATTN_OK, nothing enqueued.
+ * Errors: NULL, SHAPE, DTYPE, ALIGN, ALIAS (o overlaps S or z, or S overlaps
+ *   z, or q/k/v overlap S, z or o), HIP.
+ */
+linattn_status linattn_decode_step(float *S, float *z, const void *q, const void *k, const void *v, float *o,
+                                   int BH, int C, int M, linattn_dtype dt, void *stream);
+
+/*
+ * Kernel timer (measurement support).  When enabled, the library brackets
+ * each kernel it launches with HIP events recorded on the launch stream and,
+ * when linattn_timer_read() is called, adds up the elapsed times per kernel
+ * name.  Reading synchronises with the recorded events.  Off by default;
+ * enabling it adds two event records per kernel.
+ */
+void linattn_timer_enable(int on);
+void linattn_timer_reset(void);
+/* Total milliseconds and launch count recorded for `kernel` (a name printed
+ * by linattn_timer_names).  Returns 0 if found, -1 otherwise. */
+int linattn_timer_read(const char *kernel, double *total_ms, long *launches);
+/* Writes the ';'-separated kernel names seen so far into buf (NUL-terminated,
+ * truncated to len).  Returns the full length needed. */
+size_t linattn_timer_names(char *buf, size_t len);
+
+/*
+ * Plan override (measurement support): forces the number of sequence
+ * segments per head used by linattn_forward (0 restores the automatic
+ * choice).  Returns the previous override.  Applies to subsequent calls
+ * process-wide.  Any value gives the same result up to fp32 rounding order.
+ */
+int linattn_set_segments(int segments_per_head);
+
+/* Segments per head the planner picks for these arguments (after override). */
+int linattn_plan_segments(int B, int H, int N, linattn_dtype dt, int causal);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

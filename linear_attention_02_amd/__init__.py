@@ -1,0 +1,268 @@
+"""Linear attention with phi(x) = elu(x) + 1 on AMD Instinct MI355X (gfx950).
+
+Thin Python binding of ``liblinattn.so`` (C ABI in ``include/linattn.h``).
+This module only checks and marshals arguments -- shapes, dtypes, device
+pointers, the current HIP stream, workspace allocation through PyTorch's
+allocator -- and calls the library; every arithmetic step runs in the HIP
+kernels.  There is no fallback: if the library is missing or no GPU is
+present, calls raise.
+
+    forward(q, k, v, causal=True)               -> o
+    forward_state(q, k, v, S0=None, z0=None)    -> (o, S_N, z_N)   causal, carries state
+    decode_step(S, z, q, k, v)                  -> o               updates S, z in place
+
+q, k: [B, H, N, 64]; v: [B, H, N, 64]; float32 or bfloat16, contiguous, CUDA.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+__all__ = ["forward", "forward_state", "decode_step", "workspace_bytes", "state_workspace_bytes", "lib",
+           "LinattnError", "timer", "set_segments", "plan_segments", "LIB_PATH", "HEADER_PATH"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblinattn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "linattn.h")
+
+F32, BF16 = 0, 1
+STATUS = {0: "LINATTN_OK", 1: "LINATTN_ERR_NULL", 2: "LINATTN_ERR_SHAPE", 3: "LINATTN_ERR_DTYPE",
+          4: "LINATTN_ERR_ALIGN", 5: "LINATTN_ERR_ALIAS", 6: "LINATTN_ERR_WORKSPACE", 7: "LINATTN_ERR_HIP",
+          8: "LINATTN_ERR_ARG"}
+
+
+class LinattnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads liblinattn.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LinattnError(8, f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                                  "or python -m linear_attention_02_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.linattn_version.restype = i
+        L.linattn_version.argtypes = []
+        L.linattn_status_string.restype = ctypes.c_char_p
+        L.linattn_status_string.argtypes = [i]
+        L.linattn_last_error.restype = ctypes.c_char_p
+        L.linattn_last_error.argtypes = []
+        L.linattn_forward_workspace_bytes.restype = sz
+        L.linattn_forward_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        L.linattn_forward_state_workspace_bytes.restype = sz
+        L.linattn_forward_state_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        L.linattn_forward.restype = i
+        L.linattn_forward.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
+        L.linattn_forward_state.restype = i
+        L.linattn_forward_state.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]
+        L.linattn_decode_step.restype = i
+        L.linattn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
+        L.linattn_timer_enable.restype = None
+        L.linattn_timer_enable.argtypes = [i]
+        L.linattn_timer_reset.restype = None
+        L.linattn_timer_reset.argtypes = []
+        L.linattn_timer_read.restype = i
+        L.linattn_timer_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                         ctypes.POINTER(ctypes.c_long)]
+        L.linattn_timer_names.restype = sz
+        L.linattn_timer_names.argtypes = [ctypes.c_char_p, sz]
+        L.linattn_set_segments.restype = i
+        L.linattn_set_segments.argtypes = [i]
+        L.linattn_plan_segments.restype = i
+        L.linattn_plan_segments.argtypes = [i, i, i, i, i]
+        _lib = L
+    return _lib
+
+
+def declared_functions() -> list:
+    """Names of the functions include/linattn.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(linattn_[a-z_0-9]+)\s*\(", text)))
+
+
+def _raise(rc: int):
+    if rc != 0:
+        msg = lib().linattn_last_error().decode()
+        raise LinattnError(rc, msg or STATUS.get(rc, str(rc)))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise LinattnError(3, f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _check_cuda(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise LinattnError(8, "tensors must be on a GPU device (no CPU fallback exists)")
+        if not t.is_contiguous():
+            raise LinattnError(8, "tensors must be contiguous")
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def workspace_bytes(B: int, H: int, N: int, dtype, causal: bool) -> int:
+    dt = F32 if str(dtype).endswith("float32") else BF16
+    return int(lib().linattn_forward_workspace_bytes(B, H, N, 64, 64, dt, int(bool(causal))))
+
+
+def state_workspace_bytes(B: int, H: int, N: int, dtype) -> int:
+    dt = F32 if str(dtype).endswith("float32") else BF16
+    return int(lib().linattn_forward_state_workspace_bytes(B, H, N, 64, 64, dt))
+
+
+def _alloc_ws(nbytes: int, device, workspace):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise LinattnError(6, f"workspace needs {nbytes} bytes")
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _shape(q, k, v):
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise LinattnError(2, f"expected q, k [B,H,N,C] and v [B,H,N,M]; got {tuple(q.shape)}, "
+                              f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise LinattnError(3, "q, k and v must share one dtype")
+    B, H, N, C = q.shape
+    return B, H, N, C, v.shape[3]
+
+
+def forward(q, k, v, causal: bool = True, out=None, workspace=None, stream=None):
+    """Chunked parallel forward; returns o [B,H,N,M] in the input dtype."""
+    torch = _torch()
+    _check_cuda(q, k, v, out)
+    B, H, N, C, M = _shape(q, k, v)
+    dt = _dt(q)
+    if out is None:
+        out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    nbytes = int(lib().linattn_forward_workspace_bytes(B, H, N, C, M, dt, int(bool(causal))))
+    ws = _alloc_ws(nbytes, q.device, workspace)
+    rc = lib().linattn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, C, M, dt, int(bool(causal)),
+                               _ptr(ws), nbytes, _stream(stream))
+    _raise(rc)
+    return out
+
+
+def forward_state(q, k, v, S0=None, z0=None, out=None, S_out=None, z_out=None, workspace=None, stream=None,
+                  return_state: bool = True):
+    """Causal forward from state (S0, z0) (zero if None); returns (o, S_N, z_N).
+
+    S0/S_out: [B*H, C, M] float32 (or [B, H, C, M]); z0/z_out: [B*H, C] float32.
+    """
+    torch = _torch()
+    _check_cuda(q, k, v, S0, z0, out, S_out, z_out)
+    B, H, N, C, M = _shape(q, k, v)
+    dt = _dt(q)
+    if out is None:
+        out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    if return_state and S_out is None:
+        S_out = torch.empty((B * H, C, M), dtype=torch.float32, device=q.device)
+        z_out = torch.empty((B * H, C), dtype=torch.float32, device=q.device)
+    for t in (S0, z0, S_out, z_out):
+        if t is not None and t.dtype != torch.float32:
+            raise LinattnError(3, "states are float32")
+    nbytes = int(lib().linattn_forward_state_workspace_bytes(B, H, N, C, M, dt))
+    ws = _alloc_ws(nbytes, q.device, workspace)
+    rc = lib().linattn_forward_state(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, C, M, dt, _ptr(S0), _ptr(z0),
+                                     _ptr(S_out), _ptr(z_out), _ptr(ws), nbytes, _stream(stream))
+    _raise(rc)
+    return out, S_out, z_out
+
+
+def decode_step(S, z, q, k, v, out=None, stream=None):
+    """One recurrent step for BH heads; S [BH,C,M] and z [BH,C] float32 are updated in place.
+
+    q, k: [BH, C]; v: [BH, M] in float32 or bfloat16.  Returns o [BH, M] float32.
+    """
+    torch = _torch()
+    _check_cuda(S, z, q, k, v, out)
+    if S.dtype != torch.float32 or z.dtype != torch.float32:
+        raise LinattnError(3, "S and z are float32")
+    BH = q.shape[0]
+    C = q.shape[-1]
+    M = v.shape[-1]
+    if k.shape != q.shape or v.shape[0] != BH or S.numel() != BH * C * M or z.numel() != BH * C:
+        raise LinattnError(2, "decode_step shape mismatch")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise LinattnError(3, "q, k and v must share one dtype")
+    dt = _dt(q)
+    if out is None:
+        out = torch.empty((BH, M), dtype=torch.float32, device=q.device)
+    rc = lib().linattn_decode_step(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), BH, C, M, dt,
+                                   _stream(stream))
+    _raise(rc)
+    return out
+
+
+class timer:
+    """Per-kernel HIP-event timing inside the library (measurement support)."""
+
+    @staticmethod
+    def enable(on: bool = True):
+        lib().linattn_timer_enable(int(bool(on)))
+
+    @staticmethod
+    def reset():
+        lib().linattn_timer_reset()
+
+    @staticmethod
+    def read(kernel: str) -> Tuple[float, int]:
+        ms = ctypes.c_double(0.0)
+        n = ctypes.c_long(0)
+        if lib().linattn_timer_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)) != 0:
+            return 0.0, 0
+        return ms.value, n.value
+
+    @staticmethod
+    def names() -> list:
+        n = lib().linattn_timer_names(None, 0)
+        buf = ctypes.create_string_buffer(n + 1)
+        lib().linattn_timer_names(buf, n + 1)
+        return [s for s in buf.value.decode().split(";") if s]
+
+
+def set_segments(n: int) -> int:
+    """Forces the number of sequence segments per head (0 = automatic); returns the previous value."""
+    return int(lib().linattn_set_segments(int(n)))
+
+
+def plan_segments(B: int, H: int, N: int, dtype, causal: bool) -> int:
+    dt = F32 if str(dtype).endswith("float32") else BF16
+    return int(lib().linattn_plan_segments(B, H, N, dt, int(bool(causal))))

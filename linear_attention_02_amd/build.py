@@ -1,0 +1,70 @@
+"""Builds liblinattn.so (HIP, gfx950) in-tree.
+
+    python -m linear_attention_02_amd.build [-v]
+
+Also builds ``validate_host`` objects with the host compiler only when asked
+(``--host-check``), for sanitizer runs of the argument checks without HIP.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "liblinattn.so")
+ARCH = os.environ.get("LINATTN_ARCH", "gfx950")
+
+SOURCES = [os.path.join(CSRC, "api.hip"), os.path.join(CSRC, "validate.cpp")]
+HEADERS = [os.path.join(CSRC, f) for f in ("device_common.hpp", "forward_kernels.hpp", "decode_kernel.hpp",
+                                            "validate.hpp")] + [os.path.join(ROOT, "include", "linattn.h")]
+
+# Packed-fp32 VALU instructions are kept out of the generated code.
+HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-fno-gpu-flush-denormals-to-zero"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose: bool = False, extra=None) -> str:
+    tmp = LIB + ".tmp"
+    obj_dir = os.path.join(HERE, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    api_o = os.path.join(obj_dir, "api.o")
+    val_o = os.path.join(obj_dir, "validate.o")
+    steps = [
+        [hipcc()] + HIPCC_FLAGS + list(extra or []) + ["-c", SOURCES[0], "-o", api_o],
+        ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-c", SOURCES[1], "-o", val_o],
+        [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", api_o, val_o, "-o", tmp],
+    ]
+    for cmd in steps:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def build_host_check(out_dir: str, sanitize: bool = True) -> str:
+    """Compiles validate.cpp plus a C++ driver with g++ (no HIP), for sanitizer runs."""
+    driver = os.path.join(ROOT, "tests", "host_validate_main.cpp")
+    exe = os.path.join(out_dir, "host_validate")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-I", os.path.join(ROOT, "include"), os.path.join(CSRC, "validate.cpp"),
+           driver, "-o", exe]
+    if sanitize:
+        cmd[1:1] = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer"]
+    subprocess.run(cmd, check=True)
+    return exe
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv, extra=[a for a in sys.argv[1:] if a.startswith("-R")])

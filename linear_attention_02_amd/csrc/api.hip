@@ -1,0 +1,346 @@
+// api.hip -- the C ABI of liblinattn.so (declared in include/linattn.h).
+//
+// Host side only: validate arguments, plan the launch, enqueue kernels on the
+// caller's stream.  All arithmetic runs in the kernels of forward_kernels.hpp
+// and decode_kernel.hpp.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/linattn.h"
+#include "decode_kernel.hpp"
+#include "forward_kernels.hpp"
+#include "validate.hpp"
+
+using namespace linattn;
+
+namespace {
+
+thread_local char g_error[512] = {0};
+
+linattn_status set_status(linattn_status s, const std::string &msg) {
+  if (s == LINATTN_OK) {
+    g_error[0] = 0;
+  } else {
+    std::snprintf(g_error, sizeof g_error, "%s: %s", linattn_status_string(s), msg.c_str());
+  }
+  return s;
+}
+
+linattn_status from_check(const Check &c) { return set_status(c.status, c.message); }
+
+// --- device attribute cache -------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int compute_units() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = g_cus[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  g_cus[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+std::atomic<int> g_segment_override{0};
+
+// --- kernel timer -----------------------------------------------------------
+struct PendingEvent {
+  std::string name;
+  hipEvent_t start, stop;
+};
+std::mutex g_timer_mu;
+std::atomic<bool> g_timer_on{false};
+std::vector<PendingEvent> g_pending;
+std::map<std::string, std::pair<double, long>> g_totals;
+
+struct TimerScope {
+  bool active = false;
+  PendingEvent ev;
+  hipStream_t stream;
+  TimerScope(const char *name, hipStream_t s) : stream(s) {
+    if (!g_timer_on.load(std::memory_order_relaxed)) return;
+    ev.name = name;
+    if (hipEventCreate(&ev.start) != hipSuccess) return;
+    if (hipEventCreate(&ev.stop) != hipSuccess) {
+      (void)hipEventDestroy(ev.start);
+      return;
+    }
+    active = hipEventRecord(ev.start, stream) == hipSuccess;
+  }
+  ~TimerScope() {
+    if (!active) return;
+    (void)hipEventRecord(ev.stop, stream);
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    g_pending.push_back(ev);
+  }
+};
+
+linattn_status launch_error(const char *what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_status(LINATTN_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return LINATTN_OK;
+}
+
+const char *kname(const char *base, linattn_dtype dt) {
+  static thread_local std::string s;
+  s = std::string(base) + (dt == LINATTN_BF16 ? "_bf16" : "_f32");
+  return s.c_str();
+}
+
+template <class E>
+linattn_status run_forward(const FwdParams &base, const Plan &plan, int causal, hipStream_t stream,
+                           linattn_dtype dt) {
+  FwdParams p = base;
+  p.segments = plan.segments;
+  p.seg_chunks = plan.seg_chunks;
+  p.records = plan.records;
+  const unsigned heads = (unsigned)plan.heads;
+  const unsigned scan_blocks = (unsigned)((plan.heads * kStateFloats + 255) / 256);
+  if (causal) {
+    if (plan.segments > 1) {
+      {
+        TimerScope t(kname("seg_totals", dt), stream);
+        hipLaunchKernelGGL(seg_totals_kernel<E>, dim3(heads * (unsigned)(plan.segments - 1)), dim3(64), 0, stream,
+                           p, plan.segments - 1);
+      }
+      if (launch_error("seg_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
+      {
+        TimerScope t("scan", stream);
+        hipLaunchKernelGGL(scan_kernel, dim3(scan_blocks), dim3(256), 0, stream, p, 1);
+      }
+      if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
+      p.init = kInitRecord;
+    } else {
+      p.init = p.S0 != nullptr ? kInitNatural : kInitZero;
+    }
+    {
+      TimerScope t(kname("causal_walk", dt), stream);
+      hipLaunchKernelGGL(causal_walk_kernel<E>, dim3(heads * (unsigned)plan.segments), dim3(64), 0, stream, p);
+    }
+    if (launch_error("causal_walk") != LINATTN_OK) return LINATTN_ERR_HIP;
+  } else {
+    {
+      TimerScope t(kname("seg_totals", dt), stream);
+      hipLaunchKernelGGL(seg_totals_kernel<E>, dim3(heads * (unsigned)plan.segments), dim3(64), 0, stream, p,
+                         plan.segments);
+    }
+    if (launch_error("seg_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
+    {
+      TimerScope t("scan", stream);
+      hipLaunchKernelGGL(scan_kernel, dim3(scan_blocks), dim3(256), 0, stream, p, 0);
+    }
+    if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
+    {
+      TimerScope t(kname("noncausal_read", dt), stream);
+      hipLaunchKernelGGL(noncausal_read_kernel<E>, dim3(heads * (unsigned)plan.ranges), dim3(64), 0, stream, p,
+                         plan.ranges, plan.range_chunks);
+    }
+    if (launch_error("noncausal_read") != LINATTN_OK) return LINATTN_ERR_HIP;
+  }
+  return set_status(LINATTN_OK, "");
+}
+
+// Writes S_out/z_out = S0/z0 (or zero) for every head: the N == 0 case of
+// linattn_forward_state.
+__global__ void state_copy_kernel(const float *S0, const float *z0, float *S_out, float *z_out, long long heads) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < heads * 4096) S_out[i] = S0 ? S0[i] : 0.f;
+  if (i < heads * 64) z_out[i] = z0 ? z0[i] : 0.f;
+}
+
+linattn_status forward_impl(const void *Q, const void *K, const void *V, void *O, int B, int H, int N, int C, int M,
+                            linattn_dtype dt, int causal, const float *S0, const float *z0, float *S_out,
+                            float *z_out, void *workspace, size_t workspace_bytes, void *stream) {
+  const long long heads = (long long)B * (long long)H;
+  Plan plan;
+  if (B >= 0 && H >= 0 && N >= 0)
+    plan = plan_forward(heads, N, causal, (heads > 0 && N > 0) ? compute_units() : 1, g_segment_override.load());
+  const Check c = check_forward(Q, K, V, O, B, H, N, C, M, dt, workspace, workspace_bytes,
+                                (heads > 0 && N > 0) ? plan.workspace_bytes : 0);
+  if (!c.ok()) return from_check(c);
+  const size_t eb = dtype_bytes(dt);
+  const size_t tensor_bytes = (size_t)heads * (size_t)N * 64 * eb;
+  const Check cs = check_state_args(S0, z0, S_out, z_out, B, H, Q, K, V, O, tensor_bytes, tensor_bytes, workspace,
+                                    (heads > 0 && N > 0) ? plan.workspace_bytes : 0);
+  if (!cs.ok()) return from_check(cs);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (heads == 0) return set_status(LINATTN_OK, "");
+  if (N == 0) {
+    if (S_out == nullptr) return set_status(LINATTN_OK, "");
+    const long long n = heads * 4096;
+    hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, S0, z0, S_out, z_out,
+                       heads);
+    if (launch_error("state_copy") != LINATTN_OK) return LINATTN_ERR_HIP;
+    return set_status(LINATTN_OK, "");
+  }
+  FwdParams p{};
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.O = O;
+  p.N = N;
+  p.heads = (int)heads;
+  p.ws = reinterpret_cast<float *>(workspace);
+  p.S0 = S0;
+  p.z0 = z0;
+  p.S_out = S_out;
+  p.z_out = z_out;
+  if (dt == LINATTN_BF16) return run_forward<__bf16>(p, plan, causal, s, dt);
+  return run_forward<float>(p, plan, causal, s, dt);
+}
+
+}  // namespace
+
+extern "C" {
+
+int linattn_version(void) { return 10000; }
+
+const char *linattn_status_string(linattn_status s) {
+  switch (s) {
+  case LINATTN_OK: return "LINATTN_OK";
+  case LINATTN_ERR_NULL: return "LINATTN_ERR_NULL";
+  case LINATTN_ERR_SHAPE: return "LINATTN_ERR_SHAPE";
+  case LINATTN_ERR_DTYPE: return "LINATTN_ERR_DTYPE";
+  case LINATTN_ERR_ALIGN: return "LINATTN_ERR_ALIGN";
+  case LINATTN_ERR_ALIAS: return "LINATTN_ERR_ALIAS";
+  case LINATTN_ERR_WORKSPACE: return "LINATTN_ERR_WORKSPACE";
+  case LINATTN_ERR_HIP: return "LINATTN_ERR_HIP";
+  case LINATTN_ERR_ARG: return "LINATTN_ERR_ARG";
+  }
+  return "LINATTN_UNKNOWN_STATUS";
+}
+
+const char *linattn_last_error(void) { return g_error; }
+
+size_t linattn_forward_workspace_bytes(int B, int H, int N, int C, int M, linattn_dtype dt, int causal) {
+  if (B <= 0 || H <= 0 || N <= 0 || C != 64 || M != 64 || dtype_bytes(dt) == 0) return 0;
+  const Plan p = plan_forward((long long)B * H, N, causal, compute_units(), g_segment_override.load());
+  return p.workspace_bytes == SIZE_MAX ? 0 : p.workspace_bytes;
+}
+
+size_t linattn_forward_state_workspace_bytes(int B, int H, int N, int C, int M, linattn_dtype dt) {
+  return linattn_forward_workspace_bytes(B, H, N, C, M, dt, 1);
+}
+
+linattn_status linattn_forward(const void *Q, const void *K, const void *V, void *O, int B, int H, int N, int C,
+                               int M, linattn_dtype dt, int causal, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  try {
+    return forward_impl(Q, K, V, O, B, H, N, C, M, dt, causal ? 1 : 0, nullptr, nullptr, nullptr, nullptr,
+                        workspace, workspace_bytes, stream);
+  } catch (...) {
+    return set_status(LINATTN_ERR_ARG, "internal exception");
+  }
+}
+
+linattn_status linattn_forward_state(const void *Q, const void *K, const void *V, void *O, int B, int H, int N,
+                                     int C, int M, linattn_dtype dt, const float *S0, const float *z0, float *S_out,
+                                     float *z_out, void *workspace, size_t workspace_bytes, void *stream) {
+  try {
+    return forward_impl(Q, K, V, O, B, H, N, C, M, dt, 1, S0, z0, S_out, z_out, workspace, workspace_bytes, stream);
+  } catch (...) {
+    return set_status(LINATTN_ERR_ARG, "internal exception");
+  }
+}
+
+linattn_status linattn_decode_step(float *S, float *z, const void *q, const void *k, const void *v, float *o, int BH,
+                                   int C, int M, linattn_dtype dt, void *stream) {
+  try {
+    const Check c = check_decode(S, z, q, k, v, o, BH, C, M, dt);
+    if (!c.ok()) return from_check(c);
+    if (BH == 0) return set_status(LINATTN_OK, "");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const unsigned blocks = (unsigned)((BH + 3) / 4);
+    {
+      TimerScope t(kname("decode_step", dt), s);
+      if (dt == LINATTN_BF16) {
+        hipLaunchKernelGGL(decode_step_kernel<__bf16>, dim3(blocks), dim3(256), 0, s, S, z,
+                           reinterpret_cast<const __bf16 *>(q), reinterpret_cast<const __bf16 *>(k),
+                           reinterpret_cast<const __bf16 *>(v), o, BH);
+      } else {
+        hipLaunchKernelGGL(decode_step_kernel<float>, dim3(blocks), dim3(256), 0, s, S, z,
+                           reinterpret_cast<const float *>(q), reinterpret_cast<const float *>(k),
+                           reinterpret_cast<const float *>(v), o, BH);
+      }
+    }
+    if (launch_error("decode_step") != LINATTN_OK) return LINATTN_ERR_HIP;
+    return set_status(LINATTN_OK, "");
+  } catch (...) {
+    return set_status(LINATTN_ERR_ARG, "internal exception");
+  }
+}
+
+void linattn_timer_enable(int on) { g_timer_on.store(on != 0); }
+
+void linattn_timer_reset(void) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  for (PendingEvent &e : g_pending) {
+    (void)hipEventSynchronize(e.stop);
+    (void)hipEventDestroy(e.start);
+    (void)hipEventDestroy(e.stop);
+  }
+  g_pending.clear();
+  g_totals.clear();
+}
+
+static void timer_drain_locked() {
+  for (PendingEvent &e : g_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(e.stop) == hipSuccess && hipEventElapsedTime(&ms, e.start, e.stop) == hipSuccess) {
+      auto &t = g_totals[e.name];
+      t.first += ms;
+      t.second += 1;
+    }
+    (void)hipEventDestroy(e.start);
+    (void)hipEventDestroy(e.stop);
+  }
+  g_pending.clear();
+}
+
+int linattn_timer_read(const char *kernel, double *total_ms, long *launches) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  timer_drain_locked();
+  if (kernel == nullptr) return -1;
+  auto it = g_totals.find(kernel);
+  if (it == g_totals.end()) return -1;
+  if (total_ms) *total_ms = it->second.first;
+  if (launches) *launches = it->second.second;
+  return 0;
+}
+
+size_t linattn_timer_names(char *buf, size_t len) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  timer_drain_locked();
+  std::string all;
+  for (auto &kv : g_totals) {
+    if (!all.empty()) all += ';';
+    all += kv.first;
+  }
+  if (buf && len > 0) {
+    const size_t n = all.size() < len - 1 ? all.size() : len - 1;
+    std::memcpy(buf, all.data(), n);
+    buf[n] = 0;
+  }
+  return all.size();
+}
+
+int linattn_set_segments(int segments_per_head) {
+  return g_segment_override.exchange(segments_per_head > 0 ? segments_per_head : 0);
+}
+
+int linattn_plan_segments(int B, int H, int N, linattn_dtype dt, int causal) {
+  (void)dt;
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return plan_forward((long long)B * H, N, causal, compute_units(), g_segment_override.load()).segments;
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// decode_kernel.hpp -- one recurrent decode step for many independent heads.
+//
+// Per head ("Why Replace Attention?", §7.2 steps 1-4; constant work per step,
+// §7.4):  S += phi(k) v^T,  z += phi(k),  o = phi(q)^T S / phi(q)^T z,
+// reading the state after the update.
+//
+// One wave64 owns one head; a 256-thread workgroup holds four heads.  The
+// 64x64 fp32 state is 16 KB per head and is read and written once per step,
+// so the step is bound by memory traffic (about 0.5 flop per byte).  Lane
+// (m4, cq) = (l & 15, l >> 4) holds columns 4*m4..4*m4+3 of rows 16*cq..16*cq+15,
+// so each 16-byte load or store instruction covers four whole 256-byte rows.
+// The column sums phi(q)^T S are reduced across the four row groups with
+// cross-lane shuffles; phi(q)^T z with a full-wave reduction.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace linattn {
+
+template <class E> __device__ inline float load_elem(const E *p, int i);
+template <> __device__ inline float load_elem<float>(const float *p, int i) { return p[i]; }
+template <> __device__ inline float load_elem<__bf16>(const __bf16 *p, int i) {
+  return __uint_as_float((uint32_t)(reinterpret_cast<const uint16_t *>(p)[i]) << 16);
+}
+
+template <class E>
+__global__ __launch_bounds__(256) void decode_step_kernel(float *__restrict__ S, float *__restrict__ z,
+                                                          const E *__restrict__ q, const E *__restrict__ k,
+                                                          const E *__restrict__ v, float *__restrict__ o,
+                                                          int heads) {
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (h >= heads) return;
+  const int lane = threadIdx.x & 63;
+  const int m4 = lane & 15, cq = lane >> 4;
+
+  const E *qh = q + (long long)h * kD;
+  const E *kh = k + (long long)h * kD;
+  const E *vh = v + (long long)h * kD;
+  float4 *Sh = reinterpret_cast<float4 *>(S + (long long)h * kD * kD);
+
+  // phi(k), phi(q) for this lane's 16 rows; v for its 4 columns.
+  float pk[16], pq[16];
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    pk[rr] = phi(load_elem<E>(kh, 16 * cq + rr));
+    pq[rr] = phi(load_elem<E>(qh, 16 * cq + rr));
+  }
+  const float v0 = load_elem<E>(vh, 4 * m4 + 0), v1 = load_elem<E>(vh, 4 * m4 + 1);
+  const float v2 = load_elem<E>(vh, 4 * m4 + 2), v3 = load_elem<E>(vh, 4 * m4 + 3);
+
+  // Rank-1 update S += phi(k) v^T, then the partial read phi(q)^T S.
+  float4 s[16];
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) s[rr] = Sh[(16 * cq + rr) * 16 + m4];
+  float n0 = 0.f, n1 = 0.f, n2 = 0.f, n3 = 0.f;
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    s[rr].x += pk[rr] * v0;
+    s[rr].y += pk[rr] * v1;
+    s[rr].z += pk[rr] * v2;
+    s[rr].w += pk[rr] * v3;
+    n0 += pq[rr] * s[rr].x;
+    n1 += pq[rr] * s[rr].y;
+    n2 += pq[rr] * s[rr].z;
+    n3 += pq[rr] * s[rr].w;
+  }
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) Sh[(16 * cq + rr) * 16 + m4] = s[rr];
+
+  // z += phi(k): lane l owns z[l]; den = phi(q)^T z over the whole wave.
+  float *zh = z + (long long)h * kD;
+  const float zl = zh[lane] + phi(load_elem<E>(kh, lane));
+  zh[lane] = zl;
+  float den = phi(load_elem<E>(qh, lane)) * zl;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
+
+  // Sum the four row groups' partial columns.
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+    n0 += __shfl_xor(n0, off, 64);
+    n1 += __shfl_xor(n1, off, 64);
+    n2 += __shfl_xor(n2, off, 64);
+    n3 += __shfl_xor(n3, off, 64);
+  }
+  if (cq == 0) {
+    float4 r = make_float4(n0 / den, n1 / den, n2 / den, n3 / den);
+    reinterpret_cast<float4 *>(o + (long long)h * kD)[m4] = r;
+  }
+}
+
+}  // namespace linattn

@@ -1,0 +1,266 @@
+// device_common.hpp -- register-fragment toolkit for the gfx950 linear
+// attention kernels.
+//
+// Every kernel in this library is built from 16x16 MFMA tiles.  One wave64 is
+// one independent worker; data moves between the operand and accumulator
+// layouts entirely in registers (no LDS), using two facts about CDNA MFMAs:
+//
+//   * accumulator ("C") layout of a 16x16 tile: lane l holds D[4g+r][n] for
+//     r = 0..3, where n = l & 15 and g = l >> 4;
+//   * operand layout of a 16-wide k slice: lane l holds A[n][4g+r] (A operand,
+//     row n) or B[4g+r][n] (B operand, column n), r = 0..3.
+//
+// So an accumulator tile, rounded to the operand type, *is* an operand tile
+// whose k index is the tile's row index -- the token-contracting products
+// (A V and phi(K)^T V) consume accumulators of earlier products directly.
+// Where a tile has to change orientation, multiplying it by an identity
+// matrix on the MFMA pipe transposes it exactly (one non-zero product per
+// output, accumulated in fp32).
+//
+// Feature and value columns are visited in the order pi(kt, g, r) below, so
+// that a lane's global loads and stores are 16-byte vectors over 8 adjacent
+// columns.  pi is a permutation of 0..63; every product contracts or indexes
+// with the same pi on both sides, so results are in natural order in memory.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace linattn {
+
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+
+constexpr int kWave = 64;
+constexpr int kD = 64;      // C = M = 64 features / value columns
+constexpr int kChunk = 64;  // tokens per chunk (four 16-row tiles)
+
+// Column visited by lane group g, register r, in k-tile (or column tile) kt.
+__device__ __host__ inline constexpr int pi_col(int kt, int g, int r) {
+  return 32 * (kt >> 1) + 8 * g + 4 * (kt & 1) + r;
+}
+
+__device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------------------
+// phi(x) = elu(x) + 1: x + 1 for x > 0, e^x otherwise ("Why Replace
+// Attention?", §5.3).  e^x comes from the device's expf.
+// ---------------------------------------------------------------------------
+__device__ inline float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+// bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest-even
+// (inputs here are finite).
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ inline uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Operand fragments: four consecutive-k values per lane for one 16-wide k
+// slice.  Element type E is the MFMA operand type.
+// ---------------------------------------------------------------------------
+template <class E> struct Frag;
+
+template <> struct Frag<__bf16> {
+  uint32_t w[2];  // element r lives in half (r & 1) of w[r >> 1]
+};
+template <> struct Frag<float> {
+  float v[4];
+};
+
+template <class E> __device__ inline Frag<E> frag_zero();
+template <> __device__ inline Frag<__bf16> frag_zero<__bf16>() { return {{0u, 0u}}; }
+template <> __device__ inline Frag<float> frag_zero<float>() { return {{0.f, 0.f, 0.f, 0.f}}; }
+
+// Accumulator (fp32) -> operand fragment.
+template <class E> __device__ inline Frag<E> to_frag(f32x4 a);
+template <> __device__ inline Frag<__bf16> to_frag<__bf16>(f32x4 a) {
+  return {{pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3])}};
+}
+template <> __device__ inline Frag<float> to_frag<float>(f32x4 a) { return {{a[0], a[1], a[2], a[3]}}; }
+
+// Constant B fragments: the identity (B[k][n] = [k == n]) and all-ones.
+template <class E> __device__ inline Frag<E> frag_identity(int n16, int g);
+template <> __device__ inline Frag<__bf16> frag_identity<__bf16>(int n16, int g) {
+  const uint32_t one = 0x3f80u;
+  const int d = n16 - 4 * g;  // the one register (if any) holding the 1
+  Frag<__bf16> f;
+  f.w[0] = (d == 0 ? one : 0u) | (d == 1 ? one << 16 : 0u);
+  f.w[1] = (d == 2 ? one : 0u) | (d == 3 ? one << 16 : 0u);
+  return f;
+}
+template <> __device__ inline Frag<float> frag_identity<float>(int n16, int g) {
+  const int d = n16 - 4 * g;
+  return {{d == 0 ? 1.f : 0.f, d == 1 ? 1.f : 0.f, d == 2 ? 1.f : 0.f, d == 3 ? 1.f : 0.f}};
+}
+template <class E> __device__ inline Frag<E> frag_ones();
+template <> __device__ inline Frag<__bf16> frag_ones<__bf16>() { return {{0x3f803f80u, 0x3f803f80u}}; }
+template <> __device__ inline Frag<float> frag_ones<float>() { return {{1.f, 1.f, 1.f, 1.f}}; }
+
+// ---------------------------------------------------------------------------
+// acc += A * B over a list of 16-wide k slices.
+// bf16: pairs of slices go through one v_mfma_f32_16x16x32_bf16 (a lane's 8
+// operand values are the two slices' 4 each; A and B use the same placement,
+// so the contraction pairs matching k), an odd last slice through
+// v_mfma_f32_16x16x16_bf16.  fp32: four v_mfma_f32_16x16x4_f32 per slice,
+// register r of every lane in instruction r.
+// ---------------------------------------------------------------------------
+__device__ inline f32x4 mma2_bf16(f32x4 acc, const Frag<__bf16> &a0, const Frag<__bf16> &a1,
+                                  const Frag<__bf16> &b0, const Frag<__bf16> &b1) {
+  union { uint32_t u[4]; bf16x8 v; } A, B;
+  A.u[0] = a0.w[0]; A.u[1] = a0.w[1]; A.u[2] = a1.w[0]; A.u[3] = a1.w[1];
+  B.u[0] = b0.w[0]; B.u[1] = b0.w[1]; B.u[2] = b1.w[0]; B.u[3] = b1.w[1];
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.v, B.v, acc, 0, 0, 0);
+}
+__device__ inline f32x4 mma1_bf16(f32x4 acc, const Frag<__bf16> &a, const Frag<__bf16> &b) {
+  union { uint32_t u[2]; i16x4 v; } A, B;
+  A.u[0] = a.w[0]; A.u[1] = a.w[1];
+  B.u[0] = b.w[0]; B.u[1] = b.w[1];
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A.v, B.v, acc, 0, 0, 0);
+}
+__device__ inline f32x4 mma1_f32(f32x4 acc, const Frag<float> &a, const Frag<float> &b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[0], b.v[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[1], b.v[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[2], b.v[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[3], b.v[3], acc, 0, 0, 0);
+  return acc;
+}
+
+// acc += sum_{s < n} A[s * sa] * B[s * sb].  Strides let one helper walk
+// rows or columns of small fragment arrays; every index is a compile-time
+// constant once the callers' loops are unrolled, so nothing leaves registers.
+template <class E>
+__device__ inline f32x4 mma_k(f32x4 acc, const Frag<E> *A, int sa, const Frag<E> *B, int sb, int n);
+
+template <>
+__device__ inline f32x4 mma_k<__bf16>(f32x4 acc, const Frag<__bf16> *A, int sa, const Frag<__bf16> *B, int sb,
+                                      int n) {
+  int s = 0;
+#pragma unroll
+  for (; s + 1 < n; s += 2) acc = mma2_bf16(acc, A[s * sa], A[(s + 1) * sa], B[s * sb], B[(s + 1) * sb]);
+  if (s < n) acc = mma1_bf16(acc, A[s * sa], B[s * sb]);
+  return acc;
+}
+template <>
+__device__ inline f32x4 mma_k<float>(f32x4 acc, const Frag<float> *A, int sa, const Frag<float> *B, int sb,
+                                     int n) {
+#pragma unroll
+  for (int s = 0; s < n; ++s) acc = mma1_f32(acc, A[s * sa], B[s * sb]);
+  return acc;
+}
+
+// Single-slice product (used for identity transposes).
+template <class E> __device__ inline f32x4 mma_one(f32x4 acc, const Frag<E> &a, const Frag<E> &b);
+template <> __device__ inline f32x4 mma_one<__bf16>(f32x4 acc, const Frag<__bf16> &a, const Frag<__bf16> &b) {
+  return mma1_bf16(acc, a, b);
+}
+template <> __device__ inline f32x4 mma_one<float>(f32x4 acc, const Frag<float> &a, const Frag<float> &b) {
+  return mma1_f32(acc, a, b);
+}
+
+// Re-orient a tile: the lane that holds row n of X across its registers
+// (X[n][4g+r], operand layout) receives column n instead (X[4g+r][n],
+// accumulator layout).  Computed as X * I on the MFMA pipe; exact, because
+// each output has one non-zero product (inputs are finite).
+template <class E>
+__device__ inline f32x4 transpose_tile(const Frag<E> &x, const Frag<E> &ident) {
+  return mma_one<E>(zero4(), x, ident);
+}
+
+// ---------------------------------------------------------------------------
+// Global tile I/O.  A 16-row slab of a [rows][64] matrix is read so that lane
+// (n, g) receives row n's columns pi(kt, g, 0..3) for kt = 0..3: two 8-column
+// runs, at columns 8g and 32 + 8g.
+// ---------------------------------------------------------------------------
+template <class E> struct Slab;  // raw (unconverted) data of one lane's row piece
+
+template <> struct Slab<__bf16> {
+  u32x4 h[2];  // h[x] = 8 bf16 at columns 32x + 8g
+};
+template <> struct Slab<float> {
+  f32x4 h[2][2];  // h[x][y] = 4 floats at columns 32x + 8g + 4y
+};
+
+template <class E> __device__ inline void slab_zero(Slab<E> &s);
+template <> __device__ inline void slab_zero<__bf16>(Slab<__bf16> &s) {
+  s.h[0] = u32x4{0u, 0u, 0u, 0u};
+  s.h[1] = u32x4{0u, 0u, 0u, 0u};
+}
+template <> __device__ inline void slab_zero<float>(Slab<float> &s) {
+  for (int x = 0; x < 2; ++x)
+    for (int y = 0; y < 2; ++y) s.h[x][y] = zero4();
+}
+
+// row points at the first element of the lane's row.
+template <class E> __device__ inline void slab_load(Slab<E> &s, const E *row, int g);
+template <> __device__ inline void slab_load<__bf16>(Slab<__bf16> &s, const __bf16 *row, int g) {
+  const u32x4 *p = reinterpret_cast<const u32x4 *>(row);
+  s.h[0] = __builtin_nontemporal_load(p + g);
+  s.h[1] = __builtin_nontemporal_load(p + 4 + g);
+}
+template <> __device__ inline void slab_load<float>(Slab<float> &s, const float *row, int g) {
+  const f32x4 *p = reinterpret_cast<const f32x4 *>(row);
+  s.h[0][0] = __builtin_nontemporal_load(p + 2 * g);
+  s.h[0][1] = __builtin_nontemporal_load(p + 2 * g + 1);
+  s.h[1][0] = __builtin_nontemporal_load(p + 8 + 2 * g);
+  s.h[1][1] = __builtin_nontemporal_load(p + 8 + 2 * g + 1);
+}
+
+// Slab -> 4 operand fragments (kt = 0..3), optionally through phi, optionally
+// forced to zero (rows past the end of the sequence).
+template <class E> __device__ inline void slab_to_frags(const Slab<E> &s, Frag<E> f[4], bool apply_phi);
+
+template <>
+__device__ inline void slab_to_frags<__bf16>(const Slab<__bf16> &s, Frag<__bf16> f[4], bool apply_phi) {
+  for (int x = 0; x < 2; ++x) {
+    const uint32_t w[4] = {s.h[x][0], s.h[x][1], s.h[x][2], s.h[x][3]};
+    uint32_t o[4];
+    for (int i = 0; i < 4; ++i) {
+      if (apply_phi) {
+        o[i] = pack_bf16(phi(bf16_lo(w[i])), phi(bf16_hi(w[i])));
+      } else {
+        o[i] = w[i];
+      }
+    }
+    f[2 * x].w[0] = o[0];
+    f[2 * x].w[1] = o[1];
+    f[2 * x + 1].w[0] = o[2];
+    f[2 * x + 1].w[1] = o[3];
+  }
+}
+template <>
+__device__ inline void slab_to_frags<float>(const Slab<float> &s, Frag<float> f[4], bool apply_phi) {
+  for (int x = 0; x < 2; ++x)
+    for (int y = 0; y < 2; ++y) {
+      const f32x4 v = s.h[x][y];
+      Frag<float> &d = f[2 * x + y];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) d.v[r] = apply_phi ? phi(v[r]) : v[r];
+    }
+}
+
+// Store 8 output values of one row at columns 32x + 8g (two transposed output
+// tiles 2x and 2x+1, register r = column 32x + 8g + 4y + r).
+template <class E> __device__ inline void store_row8(E *row, int g, int x, f32x4 lo, f32x4 hi);
+template <>
+__device__ inline void store_row8<__bf16>(__bf16 *row, int g, int x, f32x4 lo, f32x4 hi) {
+  const u32x4 v = {pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(hi[0], hi[1]),
+                   pack_bf16(hi[2], hi[3])};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(row) + 4 * x + g);
+}
+template <>
+__device__ inline void store_row8<float>(float *row, int g, int x, f32x4 lo, f32x4 hi) {
+  f32x4 *p = reinterpret_cast<f32x4 *>(row) + 8 * x + 2 * g;
+  __builtin_nontemporal_store(lo, p);
+  __builtin_nontemporal_store(hi, p + 1);
+}
+
+}  // namespace linattn

@@ -1,0 +1,168 @@
+// validate.cpp -- host-side argument checks and the launch planner.
+#include "validate.hpp"
+
+#include <limits.h>
+
+namespace linattn {
+
+namespace {
+
+constexpr int kChunkTokens = 64;
+constexpr size_t kStateBytes = (4096 + 64) * sizeof(float);
+// Segments shorter than this many chunks are not worth a scan record.
+constexpr long long kMinSegmentChunks = 4;
+// Workers (waves) aimed for per compute unit: one per SIMD.
+constexpr long long kWavesPerCU = 4;
+
+Check fail(linattn_status s, const std::string &msg) {
+  Check c;
+  c.status = s;
+  c.message = msg;
+  return c;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+// a * b * c into *out without overflow of size_t; false on overflow.
+bool mul3(size_t a, size_t b, size_t c, size_t *out) {
+  if (a != 0 && b > SIZE_MAX / a) return false;
+  size_t ab = a * b;
+  if (ab != 0 && c > SIZE_MAX / ab) return false;
+  *out = ab * c;
+  return true;
+}
+
+}  // namespace
+
+size_t dtype_bytes(linattn_dtype dt) {
+  switch (dt) {
+  case LINATTN_F32: return 4;
+  case LINATTN_BF16: return 2;
+  default: return 0;
+  }
+}
+
+bool overlaps(const Buffer &a, const Buffer &b) {
+  if (a.ptr == nullptr || b.ptr == nullptr || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.ptr), b0 = reinterpret_cast<uintptr_t>(b.ptr);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+Plan plan_forward(long long heads, long long N, int causal, int cus, int override_segments) {
+  Plan p;
+  p.heads = heads;
+  p.chunks = ceil_div(N, kChunkTokens);
+  if (heads <= 0 || N <= 0) return p;
+  if (cus < 1) cus = 1;
+  const long long target = kWavesPerCU * cus;
+  long long segs;
+  if (override_segments > 0) {
+    segs = override_segments;
+  } else {
+    segs = ceil_div(target, heads);
+    const long long cap = ceil_div(p.chunks, kMinSegmentChunks);
+    if (segs > cap) segs = cap;
+  }
+  if (segs > p.chunks) segs = p.chunks;
+  if (segs < 1) segs = 1;
+  if (segs > INT_MAX / 2) segs = INT_MAX / 2;
+  long long seg_chunks = ceil_div(p.chunks, segs);
+  segs = ceil_div(p.chunks, seg_chunks);  // no empty segment
+  p.segments = (int)segs;
+  p.seg_chunks = (int)seg_chunks;
+  if (causal) {
+    p.records = p.segments > 1 ? p.segments : 0;
+  } else {
+    p.records = p.segments + 1;  // partial totals, then the head's total
+    long long ranges = ceil_div(target, heads);
+    if (ranges > p.chunks) ranges = p.chunks;
+    if (ranges < 1) ranges = 1;
+    long long range_chunks = ceil_div(p.chunks, ranges);
+    p.ranges = (int)ceil_div(p.chunks, range_chunks);
+    p.range_chunks = (int)range_chunks;
+  }
+  size_t bytes = 0;
+  if (!mul3((size_t)heads, (size_t)p.records, kStateBytes, &bytes)) bytes = SIZE_MAX;
+  p.workspace_bytes = bytes;
+  return p;
+}
+
+Check check_forward(const void *Q, const void *K, const void *V, const void *O, int B, int H, int N, int C, int M,
+                    linattn_dtype dt, const void *workspace, size_t workspace_bytes, size_t workspace_needed) {
+  const size_t eb = dtype_bytes(dt);
+  if (eb == 0) return fail(LINATTN_ERR_DTYPE, "unknown element type");
+  if (B < 0 || H < 0 || N < 0) return fail(LINATTN_ERR_SHAPE, "B, H and N must be non-negative");
+  if (C != 64 || M != 64) return fail(LINATTN_ERR_SHAPE, "only C = M = 64 is supported");
+  if ((long long)B * (long long)H > INT_MAX) return fail(LINATTN_ERR_SHAPE, "B * H exceeds INT_MAX");
+  size_t elems = 0;
+  if (!mul3((size_t)B * (size_t)H, (size_t)N, 64, &elems) || elems > SIZE_MAX / eb)
+    return fail(LINATTN_ERR_SHAPE, "tensor size overflows");
+  if (elems == 0) return Check();
+  if (!Q || !K || !V || !O) return fail(LINATTN_ERR_NULL, "Q, K, V and O must be non-NULL");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+    return fail(LINATTN_ERR_ALIGN, "Q, K, V and O must be 16-byte aligned");
+  const size_t bytes = elems * eb;
+  const Buffer bq{Q, bytes, "Q"}, bk{K, bytes, "K"}, bv{V, bytes, "V"}, bo{O, bytes, "O"};
+  if (overlaps(bo, bq) || overlaps(bo, bk) || overlaps(bo, bv))
+    return fail(LINATTN_ERR_ALIAS, "O overlaps Q, K or V");
+  if (workspace_needed > 0) {
+    if (workspace_needed == SIZE_MAX) return fail(LINATTN_ERR_SHAPE, "workspace size overflows");
+    if (workspace == nullptr || workspace_bytes < workspace_needed)
+      return fail(LINATTN_ERR_WORKSPACE, "workspace needs " + std::to_string(workspace_needed) + " bytes, got " +
+                                             std::to_string(workspace ? workspace_bytes : 0));
+    if (!aligned16(workspace)) return fail(LINATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const Buffer bw{workspace, workspace_needed, "workspace"};
+    if (overlaps(bw, bq) || overlaps(bw, bk) || overlaps(bw, bv) || overlaps(bw, bo))
+      return fail(LINATTN_ERR_ALIAS, "workspace overlaps Q, K, V or O");
+  }
+  return Check();
+}
+
+Check check_state_args(const float *S0, const float *z0, const float *S_out, const float *z_out, int B, int H,
+                       const void *Q, const void *K, const void *V, const void *O, size_t qk_bytes,
+                       size_t vo_bytes, const void *workspace, size_t workspace_bytes) {
+  if ((S0 == nullptr) != (z0 == nullptr)) return fail(LINATTN_ERR_ARG, "give both S0 and z0, or neither");
+  if ((S_out == nullptr) != (z_out == nullptr)) return fail(LINATTN_ERR_ARG, "give both S_out and z_out, or neither");
+  const size_t heads = (size_t)B * (size_t)H;
+  const size_t sb = heads * 4096 * sizeof(float), zb = heads * 64 * sizeof(float);
+  if (heads == 0) return Check();
+  for (const float *p : {S0, z0, S_out, z_out})
+    if (p && !aligned16(p)) return fail(LINATTN_ERR_ALIGN, "state buffers must be 16-byte aligned");
+  const Buffer s0{S0, sb, "S0"}, z0b{z0, zb, "z0"}, so{S_out, sb, "S_out"}, zo{z_out, zb, "z_out"};
+  if (overlaps(s0, z0b) || overlaps(so, zo) || overlaps(s0, zo) || overlaps(so, z0b))
+    return fail(LINATTN_ERR_ALIAS, "S and z buffers overlap");
+  // S_out may be S0 itself (in-place), but not a partial overlap.
+  if (overlaps(so, s0) && S_out != S0) return fail(LINATTN_ERR_ALIAS, "S_out partially overlaps S0");
+  if (overlaps(zo, z0b) && z_out != z0) return fail(LINATTN_ERR_ALIAS, "z_out partially overlaps z0");
+  const Buffer io[] = {{Q, qk_bytes, "Q"}, {K, qk_bytes, "K"}, {V, vo_bytes, "V"}, {O, vo_bytes, "O"},
+                       {workspace, workspace_bytes, "workspace"}};
+  for (const Buffer &b : io)
+    for (const Buffer *s : {&s0, &z0b, &so, &zo})
+      if (overlaps(*s, b)) return fail(LINATTN_ERR_ALIAS, std::string(s->name) + " overlaps " + b.name);
+  return Check();
+}
+
+Check check_decode(const float *S, const float *z, const void *q, const void *k, const void *v, const float *o,
+                   int BH, int C, int M, linattn_dtype dt) {
+  const size_t eb = dtype_bytes(dt);
+  if (eb == 0) return fail(LINATTN_ERR_DTYPE, "unknown element type");
+  if (BH < 0) return fail(LINATTN_ERR_SHAPE, "BH must be non-negative");
+  if (C != 64 || M != 64) return fail(LINATTN_ERR_SHAPE, "only C = M = 64 is supported");
+  if (BH == 0) return Check();
+  if (!S || !z || !q || !k || !v || !o) return fail(LINATTN_ERR_NULL, "S, z, q, k, v and o must be non-NULL");
+  for (const void *p : {(const void *)S, (const void *)z, q, k, v, (const void *)o})
+    if (!aligned16(p)) return fail(LINATTN_ERR_ALIGN, "decode buffers must be 16-byte aligned");
+  const size_t n = (size_t)BH;
+  const Buffer bS{S, n * 4096 * 4, "S"}, bz{z, n * 64 * 4, "z"}, bo{o, n * 64 * 4, "o"};
+  const Buffer bq{q, n * 64 * eb, "q"}, bk{k, n * 64 * eb, "k"}, bv{v, n * 64 * eb, "v"};
+  if (overlaps(bS, bz) || overlaps(bo, bS) || overlaps(bo, bz))
+    return fail(LINATTN_ERR_ALIAS, "S, z and o must not overlap");
+  for (const Buffer *in : {&bq, &bk, &bv})
+    for (const Buffer *st : {&bS, &bz, &bo})
+      if (overlaps(*in, *st)) return fail(LINATTN_ERR_ALIAS, std::string(in->name) + " overlaps " + st->name);
+  return Check();
+}
+
+}  // namespace linattn

@@ -1,0 +1,82 @@
+// Host-only driver for validate.cpp: exercises the argument checks and the
+// planner without HIP, so they can run under AddressSanitizer and UBSan.
+#include <cstdio>
+#include <cstdlib>
+
+#include "../linear_attention_02_amd/csrc/validate.hpp"
+
+using namespace linattn;
+
+static int failures = 0;
+
+#define EXPECT(cond)                                                  \
+  do {                                                                \
+    if (!(cond)) {                                                    \
+      std::printf("FAILED %s:%d: %s\n", __FILE__, __LINE__, #cond);   \
+      ++failures;                                                     \
+    }                                                                 \
+  } while (0)
+
+static const void *P(unsigned long v) { return reinterpret_cast<const void *>(v); }
+
+int main() {
+  // Planner.
+  Plan p = plan_forward(16, 131072, 1, 256, 0);
+  EXPECT(p.segments == 64 && p.seg_chunks == 32 && p.records == 64);
+  EXPECT(p.workspace_bytes == (size_t)16 * 64 * 4160 * 4);
+  p = plan_forward(128, 3072, 1, 256, 0);
+  EXPECT(p.segments == 8 && p.seg_chunks == 6);
+  p = plan_forward(64, 4096, 0, 256, 0);
+  EXPECT(p.segments == 16 && p.records == 17 && p.ranges == 16 && p.range_chunks == 4);
+  p = plan_forward(1, 65, 1, 256, 0);  // two chunks, cannot split below 4 chunks per segment
+  EXPECT(p.segments == 1 && p.records == 0 && p.workspace_bytes == 0);
+  p = plan_forward(1, 64 * 10, 1, 256, 4);  // override
+  EXPECT(p.segments == 4 && p.seg_chunks == 3);
+  p = plan_forward(1, 64 * 10, 1, 256, 1000);  // override capped at the chunk count
+  EXPECT(p.segments == 10 && p.seg_chunks == 1);
+  p = plan_forward(0, 100, 1, 256, 0);
+  EXPECT(p.workspace_bytes == 0);
+  // Every planned segment is non-empty and the segments cover the sequence.
+  for (long long N = 1; N < 5000; N += 97)
+    for (int ovr = 0; ovr < 9; ++ovr) {
+      Plan q = plan_forward(3, N, 1, 256, ovr);
+      EXPECT((long long)(q.segments - 1) * q.seg_chunks < q.chunks);
+      EXPECT((long long)q.segments * q.seg_chunks >= q.chunks);
+    }
+
+  // Forward checks.
+  EXPECT(check_forward(P(0x10000), P(0x20000), P(0x30000), P(0x40000), 1, 1, 64, 64, 64, LINATTN_BF16, nullptr, 0,
+                       0).ok());
+  EXPECT(check_forward(nullptr, P(32), P(48), P(64), 1, 1, 64, 64, 64, LINATTN_BF16, nullptr, 0, 0).status ==
+         LINATTN_ERR_NULL);
+  EXPECT(check_forward(P(16), P(32), P(48), P(64), 1, 1, 64, 64, 32, LINATTN_BF16, nullptr, 0, 0).status ==
+         LINATTN_ERR_SHAPE);
+  EXPECT(check_forward(P(16), P(32), P(48), P(64), 1, 1, 64, 64, 64, (linattn_dtype)9, nullptr, 0, 0).status ==
+         LINATTN_ERR_DTYPE);
+  EXPECT(check_forward(P(0x10000), P(0x20000), P(0x30000), P(0x30010), 1, 1, 64, 64, 64, LINATTN_BF16, nullptr, 0,
+                       0).status == LINATTN_ERR_ALIAS);
+  EXPECT(check_forward(P(0x10000), P(0x20000), P(0x30000), P(0x40000), 1, 1, 64, 64, 64, LINATTN_BF16, nullptr, 0,
+                       100).status == LINATTN_ERR_WORKSPACE);
+  EXPECT(check_forward(P(0x10000), P(0x20000), P(0x30000), P(0x40000), 1, 1, 64, 64, 64, LINATTN_BF16, P(0x50000),
+                       100, 100).ok());
+  EXPECT(check_forward(P(16), P(32), P(48), P(64), 1 << 20, 1 << 20, 64, 64, 64, LINATTN_BF16, nullptr, 0, 0).status ==
+         LINATTN_ERR_SHAPE);
+  EXPECT(check_forward(P(16), P(32), P(48), P(64), 0x7fffffff, 0x7fffffff, 0x7fffffff, 64, 64, LINATTN_F32,
+                       nullptr, 0, 0).status == LINATTN_ERR_SHAPE);
+
+  // Decode checks.
+  const float *S = (const float *)P(0x100000), *z = (const float *)P(0x200000), *o = (const float *)P(0x300000);
+  EXPECT(check_decode(S, z, P(0x400000), P(0x500000), P(0x600000), o, 8, 64, 64, LINATTN_F32).ok());
+  EXPECT(check_decode(S, S + 16, P(0x400000), P(0x500000), P(0x600000), o, 8, 64, 64, LINATTN_F32).status ==
+         LINATTN_ERR_ALIAS);
+  EXPECT(check_decode(S, z, P(0x400000), P(0x500000), P(0x600000), z, 8, 64, 64, LINATTN_F32).status ==
+         LINATTN_ERR_ALIAS);
+
+  // Overlap helper.
+  EXPECT(overlaps({P(100), 10, "a"}, {P(109), 1, "b"}));
+  EXPECT(!overlaps({P(100), 10, "a"}, {P(110), 1, "b"}));
+  EXPECT(!overlaps({P(100), 0, "a"}, {P(100), 1, "b"}));
+
+  if (failures == 0) std::printf("all host validation checks passed\n");
+  return failures == 0 ? 0 : 1;
+}
