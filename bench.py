@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Throughput of the linear-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one causal forward (linattn_forward, bf16 storage, fp32 state)
+over the long-context workload B=2, H=8, N=131072, C=M=64: the chunk
+kernels, the segment scan and the causal walk.  `value` is whole-job
+tokens/s (B*N sequence positions per second, every head included) with the
+inputs resident in HBM.  The same run also times
+  * the recurrent decode step on 256 sequences x 8 heads for 3072 steps
+    (captured in one HIP graph, one kernel per step),
+  * the non-causal forward on B=8, H=8, N=4096,
+  * the fp64 CPU oracle on a bounded sample of the headline workload
+    (`cpu_baseline`, rank 0 only).
+`roofline` is for the dominant kernel (the causal walk): algorithmic bytes
+per launch over its average duration from HIP events recorded on the launch
+stream during the timed steps.  `traffic` comes from the committed
+rocprofv3 FETCH_SIZE / WRITE_SIZE summary when it was taken on the current
+kernel sources, else null.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal linear-attn fwd tokens/s + % HBM/MFMA roofline; decode tokens/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
+CSRC = os.path.join(ROOT, "linear_attention_02_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hpp", ".hip", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def read_counters(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if current."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        m = re.match(r"^\s*([a-z_]+)\s*=\s*(\S+)", line)
+        if m:
+            vals[m.group(1)] = m.group(2)
+    if vals.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="causal_bf16_b2h8n131072")
+    ap.add_argument("--decode-steps", type=int, default=None, help="default: the workload's 3072")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-noncausal", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16384,
+                    help="tokens per head of the headline workload the oracle runs on")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--segments", type=int, default=0, help="force segments per head (0 = planner)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def time_forward(la, torch, w, steps, warmup, segments):
+    from workloads import forward_inputs
+    q, k, v = (t.cuda() for t in forward_inputs(w))
+    out = torch.empty_like(v)
+    nbytes = la.workspace_bytes(w.B, w.H, w.N, q.dtype, w.causal)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        la.forward(q, k, v, causal=w.causal, out=out, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    la.timer.reset()
+    la.timer.enable(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        la.forward(q, k, v, causal=w.causal, out=out, workspace=ws, stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    la.timer.enable(False)
+    total_ms = start.elapsed_time(end)
+    kernels = {}
+    for name in la.timer.names():
+        ms, n = la.timer.read(name)
+        kernels[name] = {"avg_us": 1000.0 * ms / max(n, 1), "launches": n}
+    del q, k, v, out, ws
+    return total_ms / steps, kernels
+
+
+def time_decode(la, torch, w, steps):
+    from workloads import decode_inputs
+    heads = w.heads
+    log(f"decode: drawing {steps} steps of q/k/v for {heads} heads")
+    qs = torch.empty((steps, heads, w.C), dtype=torch.float32)
+    ks = torch.empty_like(qs)
+    vs = torch.empty((steps, heads, w.M), dtype=torch.float32)
+    for t in range(steps):
+        q, k, v = decode_inputs(w, t)
+        qs[t], ks[t], vs[t] = q, k, v
+    qs, ks, vs = qs.cuda(), ks.cuda(), vs.cuda()
+    outs = torch.empty((steps, heads, w.M), dtype=torch.float32, device="cuda")
+    S = torch.zeros((heads, w.C, w.M), dtype=torch.float32, device="cuda")
+    z = torch.zeros((heads, w.C), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    # Warm up on the capture stream, then capture the whole step loop.
+    with torch.cuda.stream(stream):
+        for t in range(3):
+            la.decode_step(S, z, qs[t], ks[t], vs[t], out=outs[t], stream=stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for t in range(steps):
+            la.decode_step(S, z, qs[t], ks[t], vs[t], out=outs[t], stream=torch.cuda.current_stream())
+    S.zero_()
+    z.zero_()
+    torch.cuda.synchronize()
+    g.replay()  # one untimed replay
+    torch.cuda.synchronize()
+    S.zero_()
+    z.zero_()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    del g
+    return total_ms
+
+
+def cpu_baseline(w, sample_tokens):
+    import numpy as np  # noqa: F401
+    import oracle
+    from workloads import draw_qkv, to_oracle_array
+    n = min(sample_tokens, w.N)
+    q, k, v = draw_qkv(w.B, w.H, w.N, w.C, w.M, w.dtype, w.seed, w.scale)
+    q, k, v = (to_oracle_array(t[:, :, :n].contiguous()) for t in (q, k, v))
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.forward_recurrent(q, k, v, causal=w.causal, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": w.B * n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": dt,
+            "sample": f"fp64 C oracle (causal recurrence) on the first {n} tokens of every head of {w.name} "
+                      f"(B={w.B}, H={w.H}); tokens/s counts B*{n} positions over the wall time"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Heads shard across GPUs with no communication; see the design notes.", file=sys.stderr)
+        return 2
+    import torch
+
+    import linear_attention_02_amd as la
+    from workloads import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    la.lib()
+    if args.segments:
+        la.set_segments(args.segments)
+    w = WORKLOADS[args.workload]
+    log(f"forward {w.name}: steps={args.steps} warmup={args.warmup}")
+    ms, kernels = time_forward(la, torch, w, args.steps, args.warmup, args.segments)
+    tokens_per_s = w.tokens / (ms / 1000.0)
+    eb = 2 if w.dtype == "bf16" else 4
+    head_tokens = w.B * w.H * w.N
+    alg_bytes = head_tokens * (w.C + w.C + w.M + w.M) * eb  # read Q, K, V; write O
+    alg_flops = head_tokens * 4 * w.C * w.M                  # state write 2CM + read 2CM per head-token
+    dom = f"causal_walk_{w.dtype}" if w.causal else f"noncausal_read_{w.dtype}"
+    dom_us = kernels.get(dom, {}).get("avg_us", float("nan"))
+    achieved = alg_bytes / (dom_us * 1e-6) / 1e9
+    traffic = read_counters(dom, w.name)
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "C": w.C, "M": w.M, "causal": w.causal,
+                   "segments_per_head": la.plan_segments(w.B, w.H, w.N, torch.bfloat16, w.causal),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": dom_us},
+        "forward_call": {"achieved_GBs": alg_bytes / (ms * 1e-3) / 1e9,
+                         "frac_hbm": alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "alg_TFLOPs": alg_flops / (ms * 1e-3) / 1e12,
+                         "frac_bf16_mfma": alg_flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS},
+        "kernels": kernels,
+    }
+    if not args.no_noncausal:
+        wn = WORKLOADS["noncausal_bf16_b8h8n4096"]
+        log(f"forward {wn.name}")
+        nms, nk = time_forward(la, torch, wn, max(10, args.steps), args.warmup, args.segments)
+        nbytes = wn.B * wn.H * wn.N * 256 * 2
+        result["noncausal"] = {"workload": wn.name, "ms": nms, "tokens_per_s": wn.tokens / (nms / 1000.0),
+                               "achieved_GBs": nbytes / (nms * 1e-3) / 1e9,
+                               "frac_hbm": nbytes / (nms * 1e-3) / 1e9 / HBM_PEAK_GBS, "kernels": nk}
+    if not args.no_decode:
+        wd = WORKLOADS["decode_f32_s256h8_3072steps"]
+        steps = args.decode_steps or wd.steps
+        log(f"decode {wd.name}: {steps} steps")
+        total = time_decode(la, torch, wd, steps)
+        per_step = total / steps
+        state_bytes = wd.heads * (wd.C * wd.M + wd.C) * 4 * 2
+        io_bytes = wd.heads * (wd.C + wd.C + wd.M + wd.M) * 4
+        result["decode"] = {"workload": wd.name, "steps": steps, "us_per_step": per_step * 1000.0,
+                            "tokens_per_s": wd.sequences * steps / (total / 1000.0),
+                            "state_GBs": state_bytes / (per_step * 1e-3) / 1e9,
+                            "frac_hbm_state": state_bytes / (per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                            "bytes_per_step": state_bytes + io_bytes,
+                            "note": "one kernel per step, 3072 launches replayed from one HIP graph; the 34 MB "
+                                    "state can stay in the MI355X's 256 MB last-level cache between steps"}
+    if args.copy_calibration:
+        n = 1 << 28
+        a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = {"read": 4 * n, "write": 4 * n}
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

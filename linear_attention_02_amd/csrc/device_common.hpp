@@ -32,6 +32,8 @@ typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef float f32x2 __attribute__((__vector_size__(2 * sizeof(float))));
 
 constexpr int kWave = 64;
 constexpr int kD = 64;      // C = M = 64 features / value columns
@@ -50,17 +52,14 @@ __device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // ---------------------------------------------------------------------------
 __device__ inline float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
-// bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest-even
-// (inputs here are finite).
+// bf16 <-> fp32.  Widening is exact; narrowing is the hardware's
+// round-to-nearest-even conversion of two values at once
+// (v_cvt_pk_bf16_f32).
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ inline uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // ---------------------------------------------------------------------------
@@ -134,35 +133,30 @@ __device__ inline f32x4 mma1_f32(f32x4 acc, const Frag<float> &a, const Frag<flo
   return acc;
 }
 
-// acc += sum_{s < n} A[s * sa] * B[s * sb].  Strides let one helper walk
-// rows or columns of small fragment arrays; every index is a compile-time
-// constant once the callers' loops are unrolled, so nothing leaves registers.
+// One contraction step on a pair of 16-wide k slices (k0, k1):
+//   acc += A[:, k0] B[k0, :] + A[:, k1] B[k1, :].
+// bf16: a single v_mfma_f32_16x16x32_bf16.  fp32: eight v_mfma_f32_16x16x4_f32.
+// Callers order their loops k-outer / tiles-inner, so consecutive MFMAs
+// write different accumulators and issue back to back.
 template <class E>
-__device__ inline f32x4 mma_k(f32x4 acc, const Frag<E> *A, int sa, const Frag<E> *B, int sb, int n);
-
+__device__ inline f32x4 mac2(f32x4 acc, const Frag<E> &a0, const Frag<E> &a1, const Frag<E> &b0,
+                             const Frag<E> &b1);
 template <>
-__device__ inline f32x4 mma_k<__bf16>(f32x4 acc, const Frag<__bf16> *A, int sa, const Frag<__bf16> *B, int sb,
-                                      int n) {
-  int s = 0;
-#pragma unroll
-  for (; s + 1 < n; s += 2) acc = mma2_bf16(acc, A[s * sa], A[(s + 1) * sa], B[s * sb], B[(s + 1) * sb]);
-  if (s < n) acc = mma1_bf16(acc, A[s * sa], B[s * sb]);
-  return acc;
+__device__ inline f32x4 mac2<__bf16>(f32x4 acc, const Frag<__bf16> &a0, const Frag<__bf16> &a1,
+                                     const Frag<__bf16> &b0, const Frag<__bf16> &b1) {
+  return mma2_bf16(acc, a0, a1, b0, b1);
 }
 template <>
-__device__ inline f32x4 mma_k<float>(f32x4 acc, const Frag<float> *A, int sa, const Frag<float> *B, int sb,
-                                     int n) {
-#pragma unroll
-  for (int s = 0; s < n; ++s) acc = mma1_f32(acc, A[s * sa], B[s * sb]);
-  return acc;
+__device__ inline f32x4 mac2<float>(f32x4 acc, const Frag<float> &a0, const Frag<float> &a1, const Frag<float> &b0,
+                                    const Frag<float> &b1) {
+  return mma1_f32(mma1_f32(acc, a0, b0), a1, b1);
 }
-
-// Single-slice product (used for identity transposes).
-template <class E> __device__ inline f32x4 mma_one(f32x4 acc, const Frag<E> &a, const Frag<E> &b);
-template <> __device__ inline f32x4 mma_one<__bf16>(f32x4 acc, const Frag<__bf16> &a, const Frag<__bf16> &b) {
+// Single k slice.
+template <class E> __device__ inline f32x4 mac1(f32x4 acc, const Frag<E> &a, const Frag<E> &b);
+template <> __device__ inline f32x4 mac1<__bf16>(f32x4 acc, const Frag<__bf16> &a, const Frag<__bf16> &b) {
   return mma1_bf16(acc, a, b);
 }
-template <> __device__ inline f32x4 mma_one<float>(f32x4 acc, const Frag<float> &a, const Frag<float> &b) {
+template <> __device__ inline f32x4 mac1<float>(f32x4 acc, const Frag<float> &a, const Frag<float> &b) {
   return mma1_f32(acc, a, b);
 }
 
@@ -172,7 +166,7 @@ template <> __device__ inline f32x4 mma_one<float>(f32x4 acc, const Frag<float> 
 // each output has one non-zero product (inputs are finite).
 template <class E>
 __device__ inline f32x4 transpose_tile(const Frag<E> &x, const Frag<E> &ident) {
-  return mma_one<E>(zero4(), x, ident);
+  return mac1<E>(zero4(), x, ident);
 }
 
 // ---------------------------------------------------------------------------

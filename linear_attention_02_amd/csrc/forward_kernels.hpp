@@ -23,6 +23,8 @@
 // is independent, data is exchanged only through the scan's workspace.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace linattn {
@@ -145,6 +147,121 @@ __device__ inline void chunk_load(Chunk<E> &d, const E *Qh, const E *Kh, const E
   }
 }
 
+// Walks the chunks [t_begin, t_end) of one head, calling body(chunk, t0, rows)
+// for each.
+__device__ inline int chunk_rows(long long t0, long long t_end) {
+  return (int)(t_end - t0 < kChunk ? t_end - t0 : kChunk);
+}
+
+template <class E, bool kQ, bool kKV, class Body>
+__device__ inline void stream_chunks(const E *Qh, const E *Kh, const E *Vh, long long t_begin, long long t_end,
+                                     int n16, int g, Body &&body) {
+  // Register path (fp32 storage): load a chunk, then compute it.  Latency is
+  // hidden by the other waves of the compute unit rather than by prefetch,
+  // which would need a second 192-register buffer.
+  for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
+    Chunk<E> d;
+    chunk_load<E, kQ, kKV>(d, Qh, Kh, Vh, t0, chunk_rows(t0, t_end), n16, g);
+    body(d, t0, chunk_rows(t0, t_end));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 chunk streaming through LDS.  The next chunk is fetched with
+// global_load_lds_dwordx4 (HBM -> LDS without passing through VGPRs) into a
+// wave-private staging slot while the current chunk is computed; at the top
+// of each chunk the wave reads its slot back into registers.  Lane l's 16
+// bytes of instruction i land at slot + 1024 * i + 16 * l, so every read is a
+// conflict-free ds_read_b128 of the lane's own bytes.  No other wave touches
+// the slot, so no barrier is needed -- only the wave's own wait counters.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Slot layout: [tensor][it 4][x 2][lane 64] x 16 B; tensors in the order
+// they are loaded (Q first when present).
+template <bool kQ, bool kKV> struct StageShape {
+  static constexpr int kTensors = (kQ ? 1 : 0) + (kKV ? 2 : 0);
+  static constexpr int kVec = kTensors * 8 * 64;  // 16-byte vectors per slot
+  static constexpr int kLoadsPerChunk = kTensors * 8;
+};
+
+// s_waitcnt with only vmcnt set (expcnt, lgkmcnt left at "no wait").
+template <int N> __device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <bool kQ, bool kKV>
+__device__ inline void stage_issue(u32x4 *slot, const __bf16 *Qh, const __bf16 *Kh, const __bf16 *Vh, long long t0,
+                                   int rows, int n16, int g) {
+  const __bf16 *src[3] = {kQ ? Qh : Kh, kQ ? Kh : Vh, Vh};
+#pragma unroll
+  for (int tsr = 0; tsr < StageShape<kQ, kKV>::kTensors; ++tsr) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int row = 16 * it + n16;
+      if (row < rows) {
+        const u32x4 *gp = reinterpret_cast<const u32x4 *>(src[tsr] + (t0 + row) * kD);
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+          __builtin_amdgcn_global_load_lds(gp + 4 * x + g, (lds_void *)(slot + ((tsr * 4 + it) * 2 + x) * 64), 16,
+                                           0, 0);
+      }
+    }
+  }
+}
+
+// Reads the slot back.  Rows past the end of the sequence (only in a
+// partial last chunk) hold stale bytes: K and V rows are zeroed there, Q rows
+// are left as they are because their outputs are never stored.
+template <bool kQ, bool kKV>
+__device__ inline void stage_read(const u32x4 *slot, Chunk<__bf16> &d, int rows, int lane, int n16) {
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    Slab<__bf16> *dst[3] = {kQ ? &d.q[it] : &d.k[it], kQ ? &d.k[it] : &d.v[it], &d.v[it]};
+#pragma unroll
+    for (int tsr = 0; tsr < StageShape<kQ, kKV>::kTensors; ++tsr)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) dst[tsr]->h[x] = slot[((tsr * 4 + it) * 2 + x) * 64 + lane];
+  }
+  if (kKV && rows < kChunk) {  // uniform branch
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+      if (16 * it + n16 >= rows) {
+        slab_zero<__bf16>(d.k[it]);
+        slab_zero<__bf16>(d.v[it]);
+      }
+  }
+}
+
+// kStores: vector-memory stores body() issues per full chunk (the outputs).
+template <bool kQ, bool kKV, int kStores, class Body>
+__device__ inline void stream_chunks_lds(u32x4 *slot, const __bf16 *Qh, const __bf16 *Kh, const __bf16 *Vh,
+                                         long long t_begin, long long t_end, int lane, int n16, int g, Body &&body) {
+  if (t_begin >= t_end) return;
+  stage_issue<kQ, kKV>(slot, Qh, Kh, Vh, t_begin, chunk_rows(t_begin, t_end), n16, g);
+  for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
+    const int rows = chunk_rows(t0, t_end);
+    // Outstanding vector-memory operations: this chunk's loads, then the
+    // previous chunk's kStores output stores (every chunk but the last is
+    // full, so it issued all of them).  They retire in order, so waiting
+    // down to kStores leaves only stores in flight.  The first chunk has no
+    // stores behind its loads.
+    if (t0 == t_begin) {
+      wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<kStores>();
+    }
+    Chunk<__bf16> d;
+    stage_read<kQ, kKV>(slot, d, rows, lane, n16);
+    // The slot is refilled only after every lane's read of it returned.
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    const long long t1 = t0 + kChunk;
+    if (t1 < t_end) stage_issue<kQ, kKV>(slot, Qh, Kh, Vh, t1, chunk_rows(t1, t_end), n16, g);
+    body(d, t0, rows);
+  }
+}
+
 // phi(K) fragments (zero for rows past the end, where phi(0) = 1 would
 // otherwise leak into the sums) and V re-oriented for token contraction:
 // vb[jt][mt] is the B operand with k = token 4g+r of tile jt and column n
@@ -177,10 +294,14 @@ __device__ inline void state_update(State &st, const Frag<E> kf[4][4], const Fra
     for (int ct = 0; ct < 4; ++ct) kt_f[jt][ct] = to_frag<E>(transpose_tile<E>(kf[jt][ct], ident));
   const Frag<E> ones = frag_ones<E>();
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
+  for (int jp = 0; jp < 2; ++jp) {  // pairs of key tiles
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) st.S[ct][mt] = mma_k<E>(st.S[ct][mt], &kt_f[0][ct], 4, &vb[0][mt], 4, 4);
-    st.z[ct] = mma_k<E>(st.z[ct], &kt_f[0][ct], 4, &ones, 0, 4);
+    for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        st.S[ct][mt] = mac2<E>(st.S[ct][mt], kt_f[2 * jp][ct], kt_f[2 * jp + 1][ct], vb[2 * jp][mt], vb[2 * jp + 1][mt]);
+      st.z[ct] = mac2<E>(st.z[ct], kt_f[2 * jp][ct], kt_f[2 * jp + 1][ct], ones, ones);
+    }
   }
 }
 
@@ -190,14 +311,12 @@ __device__ inline void state_update(State &st, const Frag<E> kf[4][4], const Fra
 template <class E>
 __device__ inline void store_block(E *Oh, long long row0, int rows_left, const f32x4 num[4], f32x4 den, int n16,
                                    int g, const Frag<E> &ident) {
+  f32x4 rden;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) rden[r] = __builtin_amdgcn_rcpf(den[r]);
   f32x4 ot[4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    f32x4 o;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) o[r] = num[mt][r] / den[r];
-    ot[mt] = transpose_tile<E>(to_frag<E>(o), ident);
-  }
+  for (int mt = 0; mt < 4; ++mt) ot[mt] = transpose_tile<E>(to_frag<E>(num[mt] * rden), ident);
   if (n16 < rows_left) {
     E *row = Oh + (row0 + n16) * kD;
     store_row8<E>(row, g, 0, ot[0], ot[1]);
@@ -226,16 +345,17 @@ __global__ __launch_bounds__(64, 1) void seg_totals_kernel(FwdParams p, int tota
 
   State st;
   state_zero(st);
-  Chunk<E> cur, nxt;
-  chunk_load<E, false, true>(cur, nullptr, Kh, Vh, t_begin, (int)min<long long>(kChunk, t_end - t_begin), n16, g);
-  for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
-    const int rows = (int)min<long long>(kChunk, t_end - t0);
-    const long long t1 = t0 + kChunk;
-    if (t1 < t_end) chunk_load<E, false, true>(nxt, nullptr, Kh, Vh, t1, (int)min<long long>(kChunk, t_end - t1), n16, g);
+  auto body = [&](const Chunk<E> &d, long long t0, int rows) {
+    (void)t0;
     Frag<E> kf[4][4], vb[4][4];
-    kv_frags<E>(cur, rows, n16, ident, kf, vb);
+    kv_frags<E>(d, rows, n16, ident, kf, vb);
     state_update<E>(st, kf, vb, ident);
-    cur = nxt;
+  };
+  if constexpr (std::is_same<E, __bf16>::value) {
+    __shared__ u32x4 slot[StageShape<false, true>::kVec];
+    stream_chunks_lds<false, true, 0>(slot, nullptr, Kh, Vh, t_begin, t_end, lane, n16, g, body);
+  } else {
+    stream_chunks<E, false, true>(nullptr, Kh, Vh, t_begin, t_end, n16, g, body);
   }
   float *rec = p.ws + ((long long)h * p.records + s) * kStateFloats;
   state_store_record(st, rec, lane, n16, g);
@@ -270,15 +390,32 @@ __global__ __launch_bounds__(256) void scan_kernel(FwdParams p, int causal) {
         run = p.z0[(long long)h * 64 + pi_col(ct, g, r)];
       }
     }
-    for (int s = 0; s + 1 < P; ++s) {
-      const float t = recs[(long long)s * kStateFloats];
-      recs[(long long)s * kStateFloats] = run;
-      run += t;
+    // The loads do not depend on the running sum: issue a batch of them,
+    // then do the dependent stores, so each batch costs one memory latency.
+    constexpr int kBatch = 32;
+    for (int s0 = 0; s0 + 1 < P; s0 += kBatch) {
+      float t[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (s0 + u + 1 < P) t[u] = recs[(long long)(s0 + u) * kStateFloats];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (s0 + u + 1 < P) {
+          recs[(long long)(s0 + u) * kStateFloats] = run;
+          run += t[u];
+        }
     }
     recs[(long long)(P - 1) * kStateFloats] = run;
   } else {
     float run = 0.f;
-    for (int s = 0; s < P; ++s) run += recs[(long long)s * kStateFloats];
+    constexpr int kBatch = 32;
+    for (int s0 = 0; s0 < P; s0 += kBatch) {
+      float t[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) t[u] = s0 + u < P ? recs[(long long)(s0 + u) * kStateFloats] : 0.f;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) run += t[u];
+    }
     recs[(long long)P * kStateFloats] = run;
   }
 }
@@ -304,31 +441,48 @@ __device__ inline void causal_chunk(State &st, const Chunk<E> &d, int rows, E *O
   }
   const Frag<E> ones = frag_ones<E>();
 
+  // All four row tiles are computed even in a partial last chunk (rows past
+  // the end read zeros and are not stored), keeping the loop branch-free.
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    if (16 * it >= rows) break;
-    f32x4 num[4], den = zero4();
+    f32x4 num[4] = {zero4(), zero4(), zero4(), zero4()};
+    f32x4 den = zero4();
     // Inter-chunk read: phi(Q) S_prev and phi(Q) z_prev.
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) num[mt] = mma_k<E>(zero4(), qf[it], 1, &sb[0][mt], 4, 4);
-    den = mma_k<E>(den, qf[it], 1, zb, 1, 4);
+    for (int kp = 0; kp < 2; ++kp) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        num[mt] = mac2<E>(num[mt], qf[it][2 * kp], qf[it][2 * kp + 1], sb[2 * kp][mt], sb[2 * kp + 1][mt]);
+      den = mac2<E>(den, qf[it][2 * kp], qf[it][2 * kp + 1], zb[2 * kp], zb[2 * kp + 1]);
+    }
     // Intra-chunk: A = tril(phi(Q) phi(K)^T) for key tiles jt <= it.  The
     // product phi(K) phi(Q)^T leaves lane (n, g) with A[i = n][j = 4g+r],
     // which is already the A operand of A V (k = key token).
+    f32x4 at[4];
+#pragma unroll
+    for (int jt = 0; jt <= it; ++jt) at[jt] = zero4();
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+      for (int jt = 0; jt <= it; ++jt)
+        at[jt] = mac2<E>(at[jt], kf[jt][2 * kp], kf[jt][2 * kp + 1], qf[it][2 * kp], qf[it][2 * kp + 1]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * g + r > n16) at[it][r] = 0.f;  // inclusive mask j <= i ("Why Replace Attention?", §7.1)
     Frag<E> af[4];
 #pragma unroll
-    for (int jt = 0; jt <= it; ++jt) {
-      f32x4 at = mma_k<E>(zero4(), kf[jt], 1, qf[it], 1, 4);
-      if (jt == it) {
+    for (int jt = 0; jt <= it; ++jt) af[jt] = to_frag<E>(at[jt]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (4 * g + r > n16) at[r] = 0.f;  // inclusive mask j <= i ("Why Replace Attention?", §7.1)
-      }
-      af[jt] = to_frag<E>(at);
+    for (int jp = 0; 2 * jp + 1 <= it; ++jp) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) num[mt] = mac2<E>(num[mt], af[2 * jp], af[2 * jp + 1], vb[2 * jp][mt], vb[2 * jp + 1][mt]);
+      den = mac2<E>(den, af[2 * jp], af[2 * jp + 1], ones, ones);
     }
+    if ((it & 1) == 0) {  // odd number of key tiles: the diagonal one alone
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) num[mt] = mma_k<E>(num[mt], af, 1, &vb[0][mt], 4, it + 1);
-    den = mma_k<E>(den, af, 1, &ones, 0, it + 1);
+      for (int mt = 0; mt < 4; ++mt) num[mt] = mac1<E>(num[mt], af[it], vb[it][mt]);
+      den = mac1<E>(den, af[it], ones);
+    }
     store_block<E>(Oh, t0 + 16 * it, rows - 16 * it, num, den, n16, g, ident);
   }
   state_update<E>(st, kf, vb, ident);
@@ -361,15 +515,12 @@ __global__ __launch_bounds__(64, 1) void causal_walk_kernel(FwdParams p) {
     state_zero(st);
   }
 
-  Chunk<E> cur, nxt;
-  if (t_begin < t_end)
-    chunk_load<E, true, true>(cur, Qh, Kh, Vh, t_begin, (int)min<long long>(kChunk, t_end - t_begin), n16, g);
-  for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
-    const int rows = (int)min<long long>(kChunk, t_end - t0);
-    const long long t1 = t0 + kChunk;
-    if (t1 < t_end) chunk_load<E, true, true>(nxt, Qh, Kh, Vh, t1, (int)min<long long>(kChunk, t_end - t1), n16, g);
-    causal_chunk<E>(st, cur, rows, Oh, t0, n16, g, ident);
-    cur = nxt;
+  auto body = [&](const Chunk<E> &d, long long t0, int rows) { causal_chunk<E>(st, d, rows, Oh, t0, n16, g, ident); };
+  if constexpr (std::is_same<E, __bf16>::value) {
+    __shared__ u32x4 slot[StageShape<true, true>::kVec];
+    stream_chunks_lds<true, true, 8>(slot, Qh, Kh, Vh, t_begin, t_end, lane, n16, g, body);
+  } else {
+    stream_chunks<E, true, true>(Qh, Kh, Vh, t_begin, t_end, n16, g, body);
   }
   if (p.S_out != nullptr && s == p.segments - 1)
     state_store_natural(st, p.S_out + (long long)h * 4096, p.z_out + (long long)h * 64, n16, g);
@@ -406,26 +557,28 @@ __global__ __launch_bounds__(64, 1) void noncausal_read_kernel(FwdParams p, int 
     zb[kt] = to_frag<E>(st.z[kt]);
   }
 
-  Chunk<E> cur, nxt;
-  if (t_begin < t_end)
-    chunk_load<E, true, false>(cur, Qh, nullptr, nullptr, t_begin, (int)min<long long>(kChunk, t_end - t_begin), n16, g);
-  for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
-    const int rows = (int)min<long long>(kChunk, t_end - t0);
-    const long long t1 = t0 + kChunk;
-    if (t1 < t_end)
-      chunk_load<E, true, false>(nxt, Qh, nullptr, nullptr, t1, (int)min<long long>(kChunk, t_end - t1), n16, g);
+  auto body = [&](const Chunk<E> &d, long long t0, int rows) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      if (16 * it >= rows) break;
       Frag<E> qf[4];
-      slab_to_frags<E>(cur.q[it], qf, true);
-      f32x4 num[4];
+      slab_to_frags<E>(d.q[it], qf, true);
+      f32x4 num[4] = {zero4(), zero4(), zero4(), zero4()};
+      f32x4 den = zero4();
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) num[mt] = mma_k<E>(zero4(), qf, 1, &sb[0][mt], 4, 4);
-      const f32x4 den = mma_k<E>(zero4(), qf, 1, zb, 1, 4);
+      for (int kp = 0; kp < 2; ++kp) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          num[mt] = mac2<E>(num[mt], qf[2 * kp], qf[2 * kp + 1], sb[2 * kp][mt], sb[2 * kp + 1][mt]);
+        den = mac2<E>(den, qf[2 * kp], qf[2 * kp + 1], zb[2 * kp], zb[2 * kp + 1]);
+      }
       store_block<E>(Oh, t0 + 16 * it, rows - 16 * it, num, den, n16, g, ident);
     }
-    cur = nxt;
+  };
+  if constexpr (std::is_same<E, __bf16>::value) {
+    __shared__ u32x4 slot[StageShape<true, false>::kVec];
+    stream_chunks_lds<true, false, 8>(slot, Qh, nullptr, nullptr, t_begin, t_end, lane, n16, g, body);
+  } else {
+    stream_chunks<E, true, false>(Qh, nullptr, nullptr, t_begin, t_end, n16, g, body);
   }
 }
 
