@@ -124,7 +124,7 @@ linattn_status run_forward(const FwdParams &base, const Plan &plan, int causal, 
     }
     {
       TimerScope t(kname("causal_walk", dt), stream);
-      hipLaunchKernelGGL(causal_walk_kernel<E>, dim3(heads * (unsigned)plan.segments), dim3(64), 0, stream, p);
+      hipLaunchKernelGGL(WalkKernel<E>::fn, dim3(heads * (unsigned)plan.segments), dim3(64), 0, stream, p);
     }
     if (launch_error("causal_walk") != LINATTN_OK) return LINATTN_ERR_HIP;
   } else {

@@ -32,6 +32,7 @@ typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef float f32x2 __attribute__((__vector_size__(2 * sizeof(float))));
 
@@ -48,9 +49,12 @@ __device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // ---------------------------------------------------------------------------
 // phi(x) = elu(x) + 1: x + 1 for x > 0, e^x otherwise ("Why Replace
-// Attention?", §5.3).  e^x comes from the device's expf.
+// Attention?", §5.3).  Because e^x >= 1 + x for every x, phi(x) is the
+// median of {x + 1, e^x, 1}: for x > 0, 1 < x + 1 <= e^x; for x <= 0,
+// x + 1 <= e^x <= 1.  That is one v_med3_f32 instead of a compare and a
+// select.  e^x is the device's exp2 of x * log2(e).
 // ---------------------------------------------------------------------------
-__device__ inline float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+__device__ inline float phi(float x) { return __builtin_amdgcn_fmed3f(x + 1.f, __expf(x), 1.f); }
 
 // bf16 <-> fp32.  Widening is exact; narrowing is the hardware's
 // round-to-nearest-even conversion of two values at once
@@ -114,16 +118,16 @@ template <> __device__ inline Frag<float> frag_ones<float>() { return {{1.f, 1.f
 // ---------------------------------------------------------------------------
 __device__ inline f32x4 mma2_bf16(f32x4 acc, const Frag<__bf16> &a0, const Frag<__bf16> &a1,
                                   const Frag<__bf16> &b0, const Frag<__bf16> &b1) {
-  union { uint32_t u[4]; bf16x8 v; } A, B;
-  A.u[0] = a0.w[0]; A.u[1] = a0.w[1]; A.u[2] = a1.w[0]; A.u[3] = a1.w[1];
-  B.u[0] = b0.w[0]; B.u[1] = b0.w[1]; B.u[2] = b1.w[0]; B.u[3] = b1.w[1];
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.v, B.v, acc, 0, 0, 0);
+  const u32x4 a = {a0.w[0], a0.w[1], a1.w[0], a1.w[1]};
+  const u32x4 b = {b0.w[0], b0.w[1], b1.w[0], b1.w[1]};
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc,
+                                                 0, 0, 0);
 }
 __device__ inline f32x4 mma1_bf16(f32x4 acc, const Frag<__bf16> &a, const Frag<__bf16> &b) {
-  union { uint32_t u[2]; i16x4 v; } A, B;
-  A.u[0] = a.w[0]; A.u[1] = a.w[1];
-  B.u[0] = b.w[0]; B.u[1] = b.w[1];
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A.v, B.v, acc, 0, 0, 0);
+  const u32x2 av = {a.w[0], a.w[1]};
+  const u32x2 bv = {b.w[0], b.w[1]};
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av), __builtin_bit_cast(i16x4, bv), acc,
+                                                   0, 0, 0);
 }
 __device__ inline f32x4 mma1_f32(f32x4 acc, const Frag<float> &a, const Frag<float> &b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[0], b.v[0], acc, 0, 0, 0);

@@ -14,6 +14,11 @@
 // to rounding.  The chunk products are dense 64x64x64 contractions and run on
 // MFMA; the state stays in fp32 MFMA accumulators for a whole segment.
 //
+// Products are laid out so that each result's accumulator tile is directly
+// the operand of the next product (see device_common.hpp); outputs are
+// computed transposed, o^T = S^T phi(Q)^T + V^T A^T, which leaves each lane
+// with 8 adjacent output columns of one token (16-byte stores).
+//
 // Parallel structure.  One wave64 is one worker and owns a (head, segment)
 // pair: a run of whole chunks it walks left to right.  Sequence segments make
 // the grid wide enough for few-head workloads; their starting states come
@@ -118,209 +123,237 @@ __device__ inline void state_store_natural(const State &st, float *S, float *z, 
 }
 
 // ---------------------------------------------------------------------------
-// Raw chunk data of one wave: 4 slabs of 16 rows for each tensor.
+// Fragments of one 64-token chunk, as the MFMA products consume them.
+//   qf[it][kt]  phi(Q), row layout: lane (n, g) holds phi(Q)[16it+n][pi(kt,g,r)]
+//   kf[jt][kt]  phi(K), row layout (A operand of phi(K) phi(Q)^T)
+//   kt[jt][ct]  phi(K), token layout: lane (n, g) holds
+//               phi(K)[16jt+4g+r][pi(ct,n>>2,n&3)] (A operand of phi(K)^T V)
+//   vt[jt][mt]  V, token layout: lane (n, g) holds V[16jt+4g+r][pi(mt,n>>2,n&3)]
+//               (B operand of phi(K)^T V, A operand of V^T A^T)
+// Key rows past the end of the sequence are zero in kf, kt and vt.
 // ---------------------------------------------------------------------------
-template <class E> struct Chunk {
-  Slab<E> q[4], k[4], v[4];
-};
-
-template <class E, bool kQ, bool kKV>
-__device__ inline void chunk_load(Chunk<E> &d, const E *Qh, const E *Kh, const E *Vh, long long t0, int rows,
-                                  int n16, int g) {
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int row = 16 * it + n16;
-    if (row < rows) {
-      const long long off = (t0 + row) * kD;
-      if (kQ) slab_load<E>(d.q[it], Qh + off, g);
-      if (kKV) {
-        slab_load<E>(d.k[it], Kh + off, g);
-        slab_load<E>(d.v[it], Vh + off, g);
-      }
-    } else {
-      if (kQ) slab_zero<E>(d.q[it]);
-      if (kKV) {
-        slab_zero<E>(d.k[it]);
-        slab_zero<E>(d.v[it]);
-      }
-    }
-  }
-}
-
-// Walks the chunks [t_begin, t_end) of one head, calling body(chunk, t0, rows)
-// for each.
 __device__ inline int chunk_rows(long long t0, long long t_end) {
   return (int)(t_end - t0 < kChunk ? t_end - t0 : kChunk);
 }
 
-template <class E, bool kQ, bool kKV, class Body>
-__device__ inline void stream_chunks(const E *Qh, const E *Kh, const E *Vh, long long t_begin, long long t_end,
-                                     int n16, int g, Body &&body) {
-  // Register path (fp32 storage): load a chunk, then compute it.  Latency is
-  // hidden by the other waves of the compute unit rather than by prefetch,
-  // which would need a second 192-register buffer.
-  for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
-    Chunk<E> d;
-    chunk_load<E, kQ, kKV>(d, Qh, Kh, Vh, t0, chunk_rows(t0, t_end), n16, g);
-    body(d, t0, chunk_rows(t0, t_end));
-  }
+// Zero the registers of a token-layout fragment whose tokens are >= rows.
+__device__ inline void mask_tokens(Frag<__bf16> &f, int tok0, int rows) {
+  if (tok0 + 0 >= rows) f.w[0] &= 0xffff0000u;
+  if (tok0 + 1 >= rows) f.w[0] &= 0x0000ffffu;
+  if (tok0 + 2 >= rows) f.w[1] &= 0xffff0000u;
+  if (tok0 + 3 >= rows) f.w[1] &= 0x0000ffffu;
+}
+__device__ inline void mask_tokens(Frag<float> &f, int tok0, int rows) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (tok0 + r >= rows) f.v[r] = 0.f;
+}
+
+template <class E> __device__ inline void phi_frag(Frag<E> &f);
+template <> __device__ inline void phi_frag<__bf16>(Frag<__bf16> &f) {
+  f.w[0] = pack_bf16(phi(bf16_lo(f.w[0])), phi(bf16_hi(f.w[0])));
+  f.w[1] = pack_bf16(phi(bf16_lo(f.w[1])), phi(bf16_hi(f.w[1])));
+}
+template <> __device__ inline void phi_frag<float>(Frag<float> &f) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) f.v[r] = phi(f.v[r]);
 }
 
 // ---------------------------------------------------------------------------
-// bf16 chunk streaming through LDS.  The next chunk is fetched with
+// bf16 path: chunks staged in LDS.  The next chunk is fetched with
 // global_load_lds_dwordx4 (HBM -> LDS without passing through VGPRs) into a
-// wave-private staging slot while the current chunk is computed; at the top
-// of each chunk the wave reads its slot back into registers.  Lane l's 16
-// bytes of instruction i land at slot + 1024 * i + 16 * l, so every read is a
-// conflict-free ds_read_b128 of the lane's own bytes.  No other wave touches
-// the slot, so no barrier is needed -- only the wave's own wait counters.
+// wave-private slot while the current chunk is computed.  Lane l's 16 bytes
+// of load instruction i land at slot + 1024 i + 16 l; instruction (tsr, it, x)
+// carries rows 16it + n, columns 32x + 8g .. +7 of tensor tsr (n = l & 15,
+// g = l >> 4).  No other wave touches the slot, so no barrier is needed --
+// only the wave's own wait counters.
+//
+// Row layout fragments are the lane's own 16 bytes (ds_read_b128).  Token
+// layout fragments come from ds_read_b64_tr_b16, which within each group of
+// 16 lanes hands output lane i, register s, element i & 3 of the 8 bytes read
+// by lane 4s + (i >> 2).  Lane (src, g) therefore reads row 16jt + 4g +
+// (src >> 2), columns pi(mt, src & 3, 0..3), and lane (n, g) receives
+// X[16jt + 4g + r][pi(mt, n >> 2, n & 3)], the token layout above.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
-// Slot layout: [tensor][it 4][x 2][lane 64] x 16 B; tensors in the order
-// they are loaded (Q first when present).
-template <bool kQ, bool kKV> struct StageShape {
-  static constexpr int kTensors = (kQ ? 1 : 0) + (kKV ? 2 : 0);
-  static constexpr int kVec = kTensors * 8 * 64;  // 16-byte vectors per slot
-  static constexpr int kLoadsPerChunk = kTensors * 8;
+template <int kTensors, int NT = 4> struct Slot {
+  static constexpr int kVec = kTensors * NT * 2 * 64;  // 16-byte vectors
+  static constexpr int kLoads = kTensors * NT * 2;     // load instructions per chunk
 };
 
-// s_waitcnt with only vmcnt set (expcnt, lgkmcnt left at "no wait").
+// s_waitcnt with only vmcnt (resp. lgkmcnt) constrained.
 template <int N> __device__ inline void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+__device__ inline void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
 
-template <bool kQ, bool kKV>
-__device__ inline void stage_issue(u32x4 *slot, const __bf16 *Qh, const __bf16 *Kh, const __bf16 *Vh, long long t0,
-                                   int rows, int n16, int g) {
-  const __bf16 *src[3] = {kQ ? Qh : Kh, kQ ? Kh : Vh, Vh};
+// Fetch rows [t0, t0 + rows) of the given tensors into the slot (chunks of
+// NT row tiles of 16 tokens).
+template <int kTensors, int NT = 4>
+__device__ inline void stage_issue(u32x4 *slot, const __bf16 *const src[kTensors], long long t0, int rows, int n16,
+                                   int g) {
 #pragma unroll
-  for (int tsr = 0; tsr < StageShape<kQ, kKV>::kTensors; ++tsr) {
+  for (int tsr = 0; tsr < kTensors; ++tsr) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < NT; ++it) {
       const int row = 16 * it + n16;
       if (row < rows) {
         const u32x4 *gp = reinterpret_cast<const u32x4 *>(src[tsr] + (t0 + row) * kD);
 #pragma unroll
         for (int x = 0; x < 2; ++x)
-          __builtin_amdgcn_global_load_lds(gp + 4 * x + g, (lds_void *)(slot + ((tsr * 4 + it) * 2 + x) * 64), 16,
+          __builtin_amdgcn_global_load_lds(gp + 4 * x + g, (lds_void *)(slot + ((tsr * NT + it) * 2 + x) * 64), 16,
                                            0, 0);
       }
     }
   }
 }
 
-// Reads the slot back.  Rows past the end of the sequence (only in a
-// partial last chunk) hold stale bytes: K and V rows are zeroed there, Q rows
-// are left as they are because their outputs are never stored.
-template <bool kQ, bool kKV>
-__device__ inline void stage_read(const u32x4 *slot, Chunk<__bf16> &d, int rows, int lane, int n16) {
+// Row layout fragments of tensor tsr, row tile it (raw, no phi).
+template <int NT = 4>
+__device__ inline void lds_row_frags(const u32x4 *slot, int tsr, int it, int lane, Frag<__bf16> f[4]) {
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    Slab<__bf16> *dst[3] = {kQ ? &d.q[it] : &d.k[it], kQ ? &d.k[it] : &d.v[it], &d.v[it]};
-#pragma unroll
-    for (int tsr = 0; tsr < StageShape<kQ, kKV>::kTensors; ++tsr)
-#pragma unroll
-      for (int x = 0; x < 2; ++x) dst[tsr]->h[x] = slot[((tsr * 4 + it) * 2 + x) * 64 + lane];
-  }
-  if (kKV && rows < kChunk) {  // uniform branch
-#pragma unroll
-    for (int it = 0; it < 4; ++it)
-      if (16 * it + n16 >= rows) {
-        slab_zero<__bf16>(d.k[it]);
-        slab_zero<__bf16>(d.v[it]);
-      }
+  for (int x = 0; x < 2; ++x) {
+    const u32x4 v = slot[((tsr * NT + it) * 2 + x) * 64 + lane];
+    f[2 * x].w[0] = v[0];
+    f[2 * x].w[1] = v[1];
+    f[2 * x + 1].w[0] = v[2];
+    f[2 * x + 1].w[1] = v[3];
   }
 }
 
-// kStores: vector-memory stores body() issues per full chunk (the outputs).
-template <bool kQ, bool kKV, int kStores, class Body>
-__device__ inline void stream_chunks_lds(u32x4 *slot, const __bf16 *Qh, const __bf16 *Kh, const __bf16 *Vh,
-                                         long long t_begin, long long t_end, int lane, int n16, int g, Body &&body) {
+// Token layout fragment of tensor tsr, token tile jt, column tile mt (raw).
+template <int NT = 4>
+__device__ inline Frag<__bf16> lds_tok_frag(const u32x4 *slot, int tsr, int jt, int mt, int lane) {
+  const int src = lane & 15, g = lane >> 4;
+  const int byte = ((tsr * NT + jt) * 2 + (mt >> 1)) * 1024 + ((src & 3) * 16 + 4 * g + (src >> 2)) * 16 + 8 * (mt & 1);
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4 *)(reinterpret_cast<__attribute__((address_space(3))) char *>((lds_void *)slot) + byte));
+  Frag<__bf16> f;
+  f.w[0] = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+  f.w[1] = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
+  return f;
+}
+
+// Walks the chunks [t_begin, t_end): body(slot, t0, rows) runs on each chunk
+// while the next one streams into the slot.  kStores is the number of
+// vector-memory stores body() issues on a full chunk.
+template <int kTensors, int kStores, class Body>
+__device__ inline void stream_lds(u32x4 *slot, const __bf16 *const src[kTensors], long long t_begin, long long t_end,
+                                  int n16, int g, Body &&body) {
   if (t_begin >= t_end) return;
-  stage_issue<kQ, kKV>(slot, Qh, Kh, Vh, t_begin, chunk_rows(t_begin, t_end), n16, g);
+  stage_issue<kTensors>(slot, src, t_begin, chunk_rows(t_begin, t_end), n16, g);
   for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
     const int rows = chunk_rows(t0, t_end);
     // Outstanding vector-memory operations: this chunk's loads, then the
-    // previous chunk's kStores output stores (every chunk but the last is
-    // full, so it issued all of them).  They retire in order, so waiting
-    // down to kStores leaves only stores in flight.  The first chunk has no
-    // stores behind its loads.
+    // previous chunk's kStores stores (every chunk but the last is full).
+    // They retire in order, so waiting down to kStores leaves only stores
+    // in flight.  The first chunk has nothing behind its loads.
     if (t0 == t_begin) {
       wait_vmcnt<0>();
     } else {
       wait_vmcnt<kStores>();
     }
-    Chunk<__bf16> d;
-    stage_read<kQ, kKV>(slot, d, rows, lane, n16);
-    // The slot is refilled only after every lane's read of it returned.
-    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    body(slot, t0, rows);  // reads the slot into registers first, then waits for lgkmcnt(0)
     const long long t1 = t0 + kChunk;
-    if (t1 < t_end) stage_issue<kQ, kKV>(slot, Qh, Kh, Vh, t1, chunk_rows(t1, t_end), n16, g);
-    body(d, t0, rows);
+    (void)t1;
   }
 }
 
-// phi(K) fragments (zero for rows past the end, where phi(0) = 1 would
-// otherwise leak into the sums) and V re-oriented for token contraction:
-// vb[jt][mt] is the B operand with k = token 4g+r of tile jt and column n
-// standing for value column pi(mt, n>>2, n&3).
-template <class E>
-__device__ inline void kv_frags(const Chunk<E> &d, int rows, int n16, const Frag<E> &ident, Frag<E> kf[4][4],
-                                Frag<E> vb[4][4]) {
+// ---------------------------------------------------------------------------
+// fp32 path: register slabs straight from global memory, one chunk at a time
+// (an fp32 chunk is twice the size; latency is hidden by the other waves).
+// ---------------------------------------------------------------------------
+template <class E> struct Chunk {
+  Slab<E> t[3][4];  // [tensor][row tile]
+};
+
+template <class E, int kTensors>
+__device__ inline void chunk_load(Chunk<E> &d, const E *const src[kTensors], long long t0, int rows, int n16, int g) {
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    slab_to_frags<E>(d.k[jt], kf[jt], true);
-    if (16 * jt + n16 >= rows) {
+  for (int tsr = 0; tsr < kTensors; ++tsr)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) kf[jt][kt] = frag_zero<E>();
+    for (int it = 0; it < 4; ++it) {
+      const int row = 16 * it + n16;
+      if (row < rows) {
+        slab_load<E>(d.t[tsr][it], src[tsr] + (t0 + row) * kD, g);
+      } else {
+        slab_zero<E>(d.t[tsr][it]);
+      }
     }
-    Frag<E> vr[4];
-    slab_to_frags<E>(d.v[jt], vr, false);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) vb[jt][mt] = to_frag<E>(transpose_tile<E>(vr[mt], ident));
-  }
 }
 
+// Token layout from row layout by an identity product (exact).
+template <class E, int NT = 4>
+__device__ inline void row_to_tok(const Frag<E> rowf[NT][4], Frag<E> tok[NT][4], const Frag<E> &ident) {
+#pragma unroll
+  for (int jt = 0; jt < NT; ++jt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) tok[jt][c] = to_frag<E>(transpose_tile<E>(rowf[jt][c], ident));
+}
+
+// ---------------------------------------------------------------------------
+// Shared math.
+// ---------------------------------------------------------------------------
 // S += phi(K_c)^T V_c and z += column sums of phi(K_c) ("Why Replace
 // Attention?", §7.2, applied to a chunk of tokens at once).
-template <class E>
-__device__ inline void state_update(State &st, const Frag<E> kf[4][4], const Frag<E> vb[4][4], const Frag<E> &ident) {
-  Frag<E> kt_f[4][4];  // [jt][ct]: A operand, row n = feature pi(ct, n>>2, n&3), k = token of tile jt
-#pragma unroll
-  for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) kt_f[jt][ct] = to_frag<E>(transpose_tile<E>(kf[jt][ct], ident));
+template <class E, int NT = 4>
+__device__ inline void state_update(State &st, const Frag<E> kt[NT][4], const Frag<E> vt[NT][4]) {
   const Frag<E> ones = frag_ones<E>();
 #pragma unroll
-  for (int jp = 0; jp < 2; ++jp) {  // pairs of key tiles
+  for (int jp = 0; jp < NT / 2; ++jp) {  // pairs of token tiles
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        st.S[ct][mt] = mac2<E>(st.S[ct][mt], kt_f[2 * jp][ct], kt_f[2 * jp + 1][ct], vb[2 * jp][mt], vb[2 * jp + 1][mt]);
-      st.z[ct] = mac2<E>(st.z[ct], kt_f[2 * jp][ct], kt_f[2 * jp + 1][ct], ones, ones);
+        st.S[ct][mt] = mac2<E>(st.S[ct][mt], kt[2 * jp][ct], kt[2 * jp + 1][ct], vt[2 * jp][mt], vt[2 * jp + 1][mt]);
+      st.z[ct] = mac2<E>(st.z[ct], kt[2 * jp][ct], kt[2 * jp + 1][ct], ones, ones);
     }
   }
 }
 
-// Normalise a 16x64 block of outputs and write it: o = num / den, rounded to
-// the output type, turned row-per-lane by an identity product and stored as
-// two 16-byte vectors per lane.
+// Operands of the state read: S as the A operand of S^T phi(Q)^T (row n =
+// value column, k = feature) and z likewise (every row equal).
+template <class E> struct StateOperands {
+  Frag<E> sa[4][4];  // [kt][mt]
+  Frag<E> za[4];     // [kt]
+};
+template <class E> __device__ inline void state_operands(const State &st, StateOperands<E> &so) {
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) so.sa[kt][mt] = to_frag<E>(st.S[kt][mt]);
+    so.za[kt] = to_frag<E>(st.z[kt]);
+  }
+}
+
+// num^T (4 tiles: value columns pi(mt, g, r), token n) and den for the 16
+// tokens of row tile qf: the state read phi(Q) S and phi(Q) z.
 template <class E>
-__device__ inline void store_block(E *Oh, long long row0, int rows_left, const f32x4 num[4], f32x4 den, int n16,
-                                   int g, const Frag<E> &ident) {
-  f32x4 rden;
+__device__ inline void state_read(const StateOperands<E> &so, const Frag<E> qf[4], f32x4 nt[4], f32x4 &dt) {
+  const Frag<E> q0 = qf[0], q1 = qf[1], q2 = qf[2], q3 = qf[3];
+  const Frag<E> z0 = so.za[0], z1 = so.za[1], z2 = so.za[2], z3 = so.za[3];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) rden[r] = __builtin_amdgcn_rcpf(den[r]);
-  f32x4 ot[4];
+  for (int mt = 0; mt < 4; ++mt) nt[mt] = mac2<E>(nt[mt], so.sa[0][mt], so.sa[1][mt], q0, q1);
+  dt = mac2<E>(dt, z0, z1, q0, q1);
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) ot[mt] = transpose_tile<E>(to_frag<E>(num[mt] * rden), ident);
-  if (n16 < rows_left) {
+  for (int mt = 0; mt < 4; ++mt) nt[mt] = mac2<E>(nt[mt], so.sa[2][mt], so.sa[3][mt], q2, q3);
+  dt = mac2<E>(dt, z2, z3, q2, q3);
+}
+
+// o = num / den for 16 tokens and store: lane (n, g) holds token n's value
+// columns pi(mt, g, r) = 32x + 8g + 4y + r for mt = 2x + y, i.e. two runs of
+// 8 adjacent columns.
+template <class E, bool kFull = false>
+__device__ inline void store_rows(E *Oh, long long row0, int rows_left, const f32x4 nt[4], f32x4 dt, int n16, int g) {
+  const float rd = __builtin_amdgcn_rcpf(dt[0]);
+  if (kFull || n16 < rows_left) {
     E *row = Oh + (row0 + n16) * kD;
-    store_row8<E>(row, g, 0, ot[0], ot[1]);
-    store_row8<E>(row, g, 1, ot[2], ot[3]);
+    store_row8<E>(row, g, 0, nt[0] * rd, nt[1] * rd);
+    store_row8<E>(row, g, 1, nt[2] * rd, nt[3] * rd);
   }
 }
 
@@ -341,21 +374,59 @@ __global__ __launch_bounds__(64, 1) void seg_totals_kernel(FwdParams p, int tota
   const long long t_begin = (long long)s * p.seg_chunks * kChunk;
   long long t_end = t_begin + (long long)p.seg_chunks * kChunk;
   if (t_end > p.N) t_end = p.N;
-  const Frag<E> ident = frag_identity<E>(n16, g);
 
   State st;
   state_zero(st);
-  auto body = [&](const Chunk<E> &d, long long t0, int rows) {
-    (void)t0;
-    Frag<E> kf[4][4], vb[4][4];
-    kv_frags<E>(d, rows, n16, ident, kf, vb);
-    state_update<E>(st, kf, vb, ident);
-  };
   if constexpr (std::is_same<E, __bf16>::value) {
-    __shared__ u32x4 slot[StageShape<false, true>::kVec];
-    stream_chunks_lds<false, true, 0>(slot, nullptr, Kh, Vh, t_begin, t_end, lane, n16, g, body);
+    __shared__ u32x4 slot[Slot<2>::kVec];
+    const __bf16 *src[2] = {Kh, Vh};
+    stream_lds<2, 0>(slot, src, t_begin, t_end, n16, g, [&](const u32x4 *sl, long long t0, int rows) {
+      (void)t0;
+      Frag<E> kt[4][4], vt[4][4];
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          kt[jt][c] = lds_tok_frag(sl, 0, jt, c, lane);
+          vt[jt][c] = lds_tok_frag(sl, 1, jt, c, lane);
+        }
+      wait_lgkmcnt0();
+      if (t0 + kChunk < t_end) stage_issue<2>(slot, src, t0 + kChunk, chunk_rows(t0 + kChunk, t_end), n16, g);
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) phi_frag<E>(kt[jt][c]);
+      if (rows < kChunk) {
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            mask_tokens(kt[jt][c], 16 * jt + 4 * g, rows);
+            mask_tokens(vt[jt][c], 16 * jt + 4 * g, rows);
+          }
+      }
+      state_update<E>(st, kt, vt);
+    });
   } else {
-    stream_chunks<E, false, true>(nullptr, Kh, Vh, t_begin, t_end, n16, g, body);
+    const Frag<E> ident = frag_identity<E>(n16, g);
+    const E *src[2] = {Kh, Vh};
+    for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
+      const int rows = chunk_rows(t0, t_end);
+      Chunk<E> d;
+      chunk_load<E, 2>(d, src, t0, rows, n16, g);
+      Frag<E> kf[4][4], vf[4][4], kt[4][4], vt[4][4];
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        slab_to_frags<E>(d.t[0][jt], kf[jt], true);
+        if (16 * jt + n16 >= rows)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) kf[jt][c] = frag_zero<E>();
+        slab_to_frags<E>(d.t[1][jt], vf[jt], false);
+      }
+      row_to_tok<E>(kf, kt, ident);
+      row_to_tok<E>(vf, vt, ident);
+      state_update<E>(st, kt, vt);
+    }
   }
   float *rec = p.ws + ((long long)h * p.records + s) * kStateFloats;
   state_store_record(st, rec, lane, n16, g);
@@ -367,8 +438,12 @@ __global__ __launch_bounds__(64, 1) void seg_totals_kernel(FwdParams p, int tota
 //               with S0/z0 (or zero); record P-1 receives the prefix of the
 //               last segment.
 //   non-causal: record P receives the sum of records 0..P-1.
-// The order of additions is fixed, so results are deterministic.
+// The loads do not depend on the running sum, so they are issued in batches
+// (one memory latency per batch) before the dependent stores.  The order of
+// additions is fixed, so results are deterministic.
 // ---------------------------------------------------------------------------
+constexpr int kScanBatch = 32;
+
 __global__ __launch_bounds__(256) void scan_kernel(FwdParams p, int causal) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const int h = (int)(idx / kStateFloats);
@@ -390,16 +465,13 @@ __global__ __launch_bounds__(256) void scan_kernel(FwdParams p, int causal) {
         run = p.z0[(long long)h * 64 + pi_col(ct, g, r)];
       }
     }
-    // The loads do not depend on the running sum: issue a batch of them,
-    // then do the dependent stores, so each batch costs one memory latency.
-    constexpr int kBatch = 32;
-    for (int s0 = 0; s0 + 1 < P; s0 += kBatch) {
-      float t[kBatch];
+    for (int s0 = 0; s0 + 1 < P; s0 += kScanBatch) {
+      float t[kScanBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u)
+      for (int u = 0; u < kScanBatch; ++u)
         if (s0 + u + 1 < P) t[u] = recs[(long long)(s0 + u) * kStateFloats];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u)
+      for (int u = 0; u < kScanBatch; ++u)
         if (s0 + u + 1 < P) {
           recs[(long long)(s0 + u) * kStateFloats] = run;
           run += t[u];
@@ -408,13 +480,12 @@ __global__ __launch_bounds__(256) void scan_kernel(FwdParams p, int causal) {
     recs[(long long)(P - 1) * kStateFloats] = run;
   } else {
     float run = 0.f;
-    constexpr int kBatch = 32;
-    for (int s0 = 0; s0 < P; s0 += kBatch) {
-      float t[kBatch];
+    for (int s0 = 0; s0 < P; s0 += kScanBatch) {
+      float t[kScanBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) t[u] = s0 + u < P ? recs[(long long)(s0 + u) * kStateFloats] : 0.f;
+      for (int u = 0; u < kScanBatch; ++u) t[u] = s0 + u < P ? recs[(long long)(s0 + u) * kStateFloats] : 0.f;
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) run += t[u];
+      for (int u = 0; u < kScanBatch; ++u) run += t[u];
     }
     recs[(long long)P * kStateFloats] = run;
   }
@@ -423,42 +494,24 @@ __global__ __launch_bounds__(256) void scan_kernel(FwdParams p, int causal) {
 // ---------------------------------------------------------------------------
 // Causal walk: outputs of one segment, starting from its prefix state.
 // ---------------------------------------------------------------------------
-template <class E>
-__device__ inline void causal_chunk(State &st, const Chunk<E> &d, int rows, E *Oh, long long t0, int n16, int g,
-                                    const Frag<E> &ident) {
-  Frag<E> qf[4][4], kf[4][4], vb[4][4];
-#pragma unroll
-  for (int it = 0; it < 4; ++it) slab_to_frags<E>(d.q[it], qf[it], true);
-  kv_frags<E>(d, rows, n16, ident, kf, vb);
-
-  // The state before this chunk, as B operands for phi(Q) S and phi(Q) z.
-  Frag<E> sb[4][4], zb[4];  // [kt][mt], [kt]
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) sb[kt][mt] = to_frag<E>(st.S[kt][mt]);
-    zb[kt] = to_frag<E>(st.z[kt]);
-  }
+template <class E, int NT, bool kFull>
+__device__ inline void causal_chunk(State &st, const Frag<E> qf[NT][4], const Frag<E> kf[NT][4],
+                                    const Frag<E> kt[NT][4], const Frag<E> vt[NT][4], int rows, E *Oh, long long t0,
+                                    int n16, int g) {
+  StateOperands<E> so;
+  state_operands<E>(st, so);  // the state before this chunk (updated at the end)
   const Frag<E> ones = frag_ones<E>();
-
-  // All four row tiles are computed even in a partial last chunk (rows past
-  // the end read zeros and are not stored), keeping the loop branch-free.
+  // All row tiles are computed even in a partial last chunk (rows past the
+  // end are not stored), keeping the tile loop branch-free.
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    f32x4 num[4] = {zero4(), zero4(), zero4(), zero4()};
-    f32x4 den = zero4();
+  for (int it = 0; it < NT; ++it) {
+    f32x4 nt[4] = {zero4(), zero4(), zero4(), zero4()};
+    f32x4 dt = zero4();
     // Inter-chunk read: phi(Q) S_prev and phi(Q) z_prev.
-#pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        num[mt] = mac2<E>(num[mt], qf[it][2 * kp], qf[it][2 * kp + 1], sb[2 * kp][mt], sb[2 * kp + 1][mt]);
-      den = mac2<E>(den, qf[it][2 * kp], qf[it][2 * kp + 1], zb[2 * kp], zb[2 * kp + 1]);
-    }
-    // Intra-chunk: A = tril(phi(Q) phi(K)^T) for key tiles jt <= it.  The
-    // product phi(K) phi(Q)^T leaves lane (n, g) with A[i = n][j = 4g+r],
-    // which is already the A operand of A V (k = key token).
-    f32x4 at[4];
+    state_read<E>(so, qf[it], nt, dt);
+    // Intra-chunk: A^T = phi(K) phi(Q)^T for key tiles jt <= it; lane (n, g)
+    // holds A[i = n][j = 4g+r], the B operand of V^T A^T (k = key token).
+    f32x4 at[NT];
 #pragma unroll
     for (int jt = 0; jt <= it; ++jt) at[jt] = zero4();
 #pragma unroll
@@ -469,27 +522,72 @@ __device__ inline void causal_chunk(State &st, const Chunk<E> &d, int rows, E *O
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (4 * g + r > n16) at[it][r] = 0.f;  // inclusive mask j <= i ("Why Replace Attention?", §7.1)
-    Frag<E> af[4];
+    Frag<E> af[NT];
 #pragma unroll
     for (int jt = 0; jt <= it; ++jt) af[jt] = to_frag<E>(at[jt]);
 #pragma unroll
     for (int jp = 0; 2 * jp + 1 <= it; ++jp) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) num[mt] = mac2<E>(num[mt], af[2 * jp], af[2 * jp + 1], vb[2 * jp][mt], vb[2 * jp + 1][mt]);
-      den = mac2<E>(den, af[2 * jp], af[2 * jp + 1], ones, ones);
+      for (int mt = 0; mt < 4; ++mt) nt[mt] = mac2<E>(nt[mt], vt[2 * jp][mt], vt[2 * jp + 1][mt], af[2 * jp], af[2 * jp + 1]);
+      dt = mac2<E>(dt, ones, ones, af[2 * jp], af[2 * jp + 1]);
     }
     if ((it & 1) == 0) {  // odd number of key tiles: the diagonal one alone
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) num[mt] = mac1<E>(num[mt], af[it], vb[it][mt]);
-      den = mac1<E>(den, af[it], ones);
+      for (int mt = 0; mt < 4; ++mt) nt[mt] = mac1<E>(nt[mt], vt[it][mt], af[it]);
+      dt = mac1<E>(dt, ones, af[it]);
     }
-    store_block<E>(Oh, t0 + 16 * it, rows - 16 * it, num, den, n16, g, ident);
+    store_rows<E, kFull>(Oh, t0 + 16 * it, rows - 16 * it, nt, dt, n16, g);
   }
-  state_update<E>(st, kf, vb, ident);
+  state_update<E, NT>(st, kt, vt);
 }
 
+// bf16 chunk body: registers from the slot, refill the slot with the next
+// chunk, then compute.  kFull: every row of the chunk is inside the sequence
+// (all chunks but possibly a segment's last), so no masking is compiled in.
+template <int NT, bool kFull>
+__device__ inline void causal_chunk_lds(State &st, u32x4 *slot, const __bf16 *const src[3], long long t0,
+                                        long long t_end, int rows, __bf16 *Oh, int lane, int n16, int g,
+                                        const Frag<__bf16> &ident) {
+  typedef __bf16 E;
+  constexpr int kT = 16 * NT;
+  Frag<E> qf[NT][4], kf[NT][4], kt[NT][4], vt[NT][4];
+#pragma unroll
+  for (int it = 0; it < NT; ++it) {
+    lds_row_frags<NT>(slot, 0, it, lane, qf[it]);
+    lds_row_frags<NT>(slot, 1, it, lane, kf[it]);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) vt[it][mt] = lds_tok_frag<NT>(slot, 2, it, mt, lane);
+  }
+  wait_lgkmcnt0();  // the slot is refilled only after every lane's read of it returned
+  if (t0 + kT < t_end) stage_issue<3, NT>(slot, src, t0 + kT, (int)min<long long>(kT, t_end - t0 - kT), n16, g);
+#pragma unroll
+  for (int it = 0; it < NT; ++it)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      phi_frag<E>(qf[it][c]);
+      phi_frag<E>(kf[it][c]);
+    }
+  if (!kFull) {
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) {
+      if (16 * jt + n16 >= rows)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kf[jt][c] = frag_zero<E>();
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mask_tokens(vt[jt][c], 16 * jt + 4 * g, rows);
+    }
+  }
+  row_to_tok<E, NT>(kf, kt, ident);
+  causal_chunk<E, NT, kFull>(st, qf, kf, kt, vt, rows, Oh, t0, n16, g);
+}
+
+// Row tiles per chunk of the bf16 walk (4: 64-token chunks).  32-token
+// chunks fit two waves per SIMD but were measured slower: the walk is bound
+// by HBM traffic either way, and smaller chunks add per-chunk work.
+constexpr int kWalkTilesBf16 = 4;
+
 template <class E>
-__global__ __launch_bounds__(64, 1) void causal_walk_kernel(FwdParams p) {
+__device__ inline void causal_walk(const FwdParams &p) {
   const int worker = blockIdx.x;
   const int h = worker % p.heads;
   const int s = worker / p.heads;
@@ -515,16 +613,60 @@ __global__ __launch_bounds__(64, 1) void causal_walk_kernel(FwdParams p) {
     state_zero(st);
   }
 
-  auto body = [&](const Chunk<E> &d, long long t0, int rows) { causal_chunk<E>(st, d, rows, Oh, t0, n16, g, ident); };
   if constexpr (std::is_same<E, __bf16>::value) {
-    __shared__ u32x4 slot[StageShape<true, true>::kVec];
-    stream_chunks_lds<true, true, 8>(slot, Qh, Kh, Vh, t_begin, t_end, lane, n16, g, body);
+    constexpr int NT = kWalkTilesBf16;
+    constexpr int kT = 16 * NT;
+    __shared__ u32x4 slot[Slot<3, NT>::kVec];
+    const __bf16 *src[3] = {Qh, Kh, Vh};
+    if (t_begin < t_end) stage_issue<3, NT>(slot, src, t_begin, (int)min<long long>(kT, t_end - t_begin), n16, g);
+    for (long long t0 = t_begin; t0 < t_end; t0 += kT) {
+      const int rows = (int)min<long long>(kT, t_end - t0);
+      // Outstanding vector-memory operations: this chunk's loads, then the
+      // previous chunk's 2*NT output stores (full chunk).  They retire in
+      // order, so waiting down to 2*NT leaves only stores in flight.
+      if (t0 == t_begin) {
+        wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<2 * NT>();
+      }
+      if (rows == kT) {
+        causal_chunk_lds<NT, true>(st, slot, src, t0, t_end, rows, Oh, lane, n16, g, ident);
+      } else {
+        causal_chunk_lds<NT, false>(st, slot, src, t0, t_end, rows, Oh, lane, n16, g, ident);
+      }
+    }
   } else {
-    stream_chunks<E, true, true>(Qh, Kh, Vh, t_begin, t_end, n16, g, body);
+    const E *src[3] = {Qh, Kh, Vh};
+    for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
+      const int rows = chunk_rows(t0, t_end);
+      Chunk<E> d;
+      chunk_load<E, 3>(d, src, t0, rows, n16, g);
+      Frag<E> qf[4][4], kf[4][4], vf[4][4], kt[4][4], vt[4][4];
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        slab_to_frags<E>(d.t[0][it], qf[it], true);
+        slab_to_frags<E>(d.t[1][it], kf[it], true);
+        if (16 * it + n16 >= rows)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) kf[it][c] = frag_zero<E>();
+        slab_to_frags<E>(d.t[2][it], vf[it], false);
+      }
+      row_to_tok<E>(kf, kt, ident);
+      row_to_tok<E>(vf, vt, ident);
+      causal_chunk<E, 4, false>(st, qf, kf, kt, vt, rows, Oh, t0, n16, g);
+    }
   }
   if (p.S_out != nullptr && s == p.segments - 1)
     state_store_natural(st, p.S_out + (long long)h * 4096, p.z_out + (long long)h * 64, n16, g);
 }
+
+// One wave per SIMD: the walk keeps the state, one chunk's fragments and the
+// products' accumulators in registers (about 400 of the 512).
+__global__ __launch_bounds__(64, 1) void causal_walk_kernel_bf16(FwdParams p) { causal_walk<__bf16>(p); }
+__global__ __launch_bounds__(64, 1) void causal_walk_kernel_f32(FwdParams p) { causal_walk<float>(p); }
+template <class E> struct WalkKernel;
+template <> struct WalkKernel<__bf16> { static constexpr auto fn = causal_walk_kernel_bf16; };
+template <> struct WalkKernel<float> { static constexpr auto fn = causal_walk_kernel_f32; };
 
 // ---------------------------------------------------------------------------
 // Non-causal pass 2: o_i = phi(q_i)^T S / phi(q_i)^T z with the head's total
@@ -545,40 +687,53 @@ __global__ __launch_bounds__(64, 1) void noncausal_read_kernel(FwdParams p, int 
   const long long t_begin = (long long)s * range_chunks * kChunk;
   long long t_end = t_begin + (long long)range_chunks * kChunk;
   if (t_end > p.N) t_end = p.N;
-  const Frag<E> ident = frag_identity<E>(n16, g);
 
   State st;
   state_load_record(st, p.ws + ((long long)h * p.records + p.segments) * kStateFloats, lane, g);
-  Frag<E> sb[4][4], zb[4];
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) sb[kt][mt] = to_frag<E>(st.S[kt][mt]);
-    zb[kt] = to_frag<E>(st.z[kt]);
-  }
-
-  auto body = [&](const Chunk<E> &d, long long t0, int rows) {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      Frag<E> qf[4];
-      slab_to_frags<E>(d.q[it], qf, true);
-      f32x4 num[4] = {zero4(), zero4(), zero4(), zero4()};
-      f32x4 den = zero4();
-#pragma unroll
-      for (int kp = 0; kp < 2; ++kp) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          num[mt] = mac2<E>(num[mt], qf[2 * kp], qf[2 * kp + 1], sb[2 * kp][mt], sb[2 * kp + 1][mt]);
-        den = mac2<E>(den, qf[2 * kp], qf[2 * kp + 1], zb[2 * kp], zb[2 * kp + 1]);
-      }
-      store_block<E>(Oh, t0 + 16 * it, rows - 16 * it, num, den, n16, g, ident);
-    }
-  };
+  StateOperands<E> so;
+  state_operands<E>(st, so);
   if constexpr (std::is_same<E, __bf16>::value) {
-    __shared__ u32x4 slot[StageShape<true, false>::kVec];
-    stream_chunks_lds<true, false, 8>(slot, Qh, nullptr, nullptr, t_begin, t_end, lane, n16, g, body);
+    __shared__ u32x4 slot[Slot<1>::kVec];
+    const __bf16 *src[1] = {Qh};
+    if (t_begin < t_end) stage_issue<1>(slot, src, t_begin, chunk_rows(t_begin, t_end), n16, g);
+    for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
+      const int rows = chunk_rows(t0, t_end);
+      if (t0 == t_begin) {  // see stream_lds
+        wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<8>();
+      }
+      Frag<E> qf[4][4];
+#pragma unroll
+      for (int it = 0; it < 4; ++it) lds_row_frags(slot, 0, it, lane, qf[it]);
+      wait_lgkmcnt0();
+      if (t0 + kChunk < t_end) stage_issue<1>(slot, src, t0 + kChunk, chunk_rows(t0 + kChunk, t_end), n16, g);
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) phi_frag<E>(qf[it][c]);
+        f32x4 nt[4] = {zero4(), zero4(), zero4(), zero4()};
+        f32x4 dt = zero4();
+        state_read<E>(so, qf[it], nt, dt);
+        store_rows<E>(Oh, t0 + 16 * it, rows - 16 * it, nt, dt, n16, g);
+      }
+    }
   } else {
-    stream_chunks<E, true, false>(Qh, nullptr, nullptr, t_begin, t_end, n16, g, body);
+    const E *src[1] = {Qh};
+    for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
+      const int rows = chunk_rows(t0, t_end);
+      Chunk<E> d;
+      chunk_load<E, 1>(d, src, t0, rows, n16, g);
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        Frag<E> qf[4];
+        slab_to_frags<E>(d.t[0][it], qf, true);
+        f32x4 nt[4] = {zero4(), zero4(), zero4(), zero4()};
+        f32x4 dt = zero4();
+        state_read<E>(so, qf, nt, dt);
+        store_rows<E>(Oh, t0 + 16 * it, rows - 16 * it, nt, dt, n16, g);
+      }
+    }
   }
 }
 

@@ -11,7 +11,8 @@ constexpr int kChunkTokens = 64;
 constexpr size_t kStateBytes = (4096 + 64) * sizeof(float);
 // Segments shorter than this many chunks are not worth a scan record.
 constexpr long long kMinSegmentChunks = 4;
-// Workers (waves) aimed for per compute unit: one per SIMD.
+// Workers (waves) aimed for per compute unit: one per SIMD (the walk kernel
+// holds about 400 registers per lane).
 constexpr long long kWavesPerCU = 4;
 
 Check fail(linattn_status s, const std::string &msg) {
