@@ -75,8 +75,8 @@ def parse_args():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-noncausal", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=16384,
-                    help="tokens per head of the headline workload the oracle runs on")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="tokens per head of the headline workload the oracle runs on (0 = all)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     ap.add_argument("--segments", type=int, default=0, help="force segments per head (0 = planner)")
@@ -87,9 +87,10 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def time_forward(la, torch, w, steps, warmup, segments):
+def time_forward(la, torch, w, steps, warmup, segments, host_inputs=None):
     from workloads import forward_inputs
-    q, k, v = (t.cuda() for t in forward_inputs(w))
+    host = host_inputs if host_inputs is not None else forward_inputs(w)
+    q, k, v = (t.cuda() for t in host)
     out = torch.empty_like(v)
     nbytes = la.workspace_bytes(w.B, w.H, w.N, q.dtype, w.causal)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
@@ -158,28 +159,27 @@ def time_decode(la, torch, w, steps):
     return total_ms
 
 
-def cpu_baseline(w, sample_tokens):
-    import numpy as np  # noqa: F401
+def cpu_baseline(w, sample_tokens, host_inputs):
     import oracle
-    from workloads import draw_qkv, to_oracle_array
-    n = min(sample_tokens, w.N)
-    q, k, v = draw_qkv(w.B, w.H, w.N, w.C, w.M, w.dtype, w.seed, w.scale)
-    q, k, v = (to_oracle_array(t[:, :, :n].contiguous()) for t in (q, k, v))
+    from workloads import to_oracle_array
+    n = w.N if sample_tokens <= 0 else min(sample_tokens, w.N)
+    q, k, v = (to_oracle_array(t[:, :, :n].contiguous()) for t in host_inputs)
     threads = oracle.default_threads()
     t0 = time.perf_counter()
     oracle.forward_recurrent(q, k, v, causal=w.causal, threads=threads)
     dt = time.perf_counter() - t0
     return {"value": w.B * n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "seconds": dt,
-            "sample": f"fp64 C oracle (causal recurrence) on the first {n} tokens of every head of {w.name} "
-                      f"(B={w.B}, H={w.H}); tokens/s counts B*{n} positions over the wall time"}
+            "sample": f"fp64 C oracle (causal recurrence, O(N) per head) on the first {n} of {w.N} tokens of every "
+                      f"head of {w.name} (B={w.B}, H={w.H}, same host inputs as the GPU run); tokens/s counts "
+                      f"B*{n} positions over the wall time, threads over (batch, head)"}
 
 
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
-              "Heads shard across GPUs with no communication; see the design notes.", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Heads shard across GPUs with no communication (each GPU would run this library on its share).", file=sys.stderr)
         return 2
     import torch
 
@@ -193,8 +193,10 @@ def main():
     if args.segments:
         la.set_segments(args.segments)
     w = WORKLOADS[args.workload]
+    from workloads import forward_inputs
+    host_inputs = forward_inputs(w)
     log(f"forward {w.name}: steps={args.steps} warmup={args.warmup}")
-    ms, kernels = time_forward(la, torch, w, args.steps, args.warmup, args.segments)
+    ms, kernels = time_forward(la, torch, w, args.steps, args.warmup, args.segments, host_inputs)
     tokens_per_s = w.tokens / (ms / 1000.0)
     eb = 2 if w.dtype == "bf16" else 4
     head_tokens = w.B * w.H * w.N
@@ -262,7 +264,7 @@ def main():
         result["copy_calibration_bytes"] = {"read": 4 * n, "write": 4 * n}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens, host_inputs)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -96,10 +96,16 @@ class using_library:
 
 
 def default_threads() -> int:
+    """Cores this process may use: its CPU affinity, capped by OMP_NUM_THREADS if set."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = max(1, len(os.sched_getaffinity(0)))
     except AttributeError:  # pragma: no cover
-        return max(1, os.cpu_count() or 1)
+        n = max(1, os.cpu_count() or 1)
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        cap = 0
+    return min(n, cap) if cap > 0 else n
 
 
 def _dtype_code(a: np.ndarray) -> int:

@@ -13,7 +13,7 @@
  *           (zhongzhoutan-coder.github.io/algorithms/attention/linear/)
  *   [PR]   "[Paper Review] Transformers are RNNs ..." (velog.io/@jmsong62)
  *
- * Conventions (readings of the pages, listed in the design doc):
+ * Conventions (readings of the pages where they leave a point open):
  *   - phi(x) = elu(x) + 1 with alpha = 1: x + 1 for x > 0, exp(x) otherwise
  *     ([WRA] §5.3, boxed formula and the elu definition under it).
  *   - causal sums are inclusive, j <= i ([WRA] §7.1).
