@@ -348,12 +348,39 @@ __device__ inline void state_read(const StateOperands<E> &so, const Frag<E> qf[4
 // columns pi(mt, g, r) = 32x + 8g + 4y + r for mt = 2x + y, i.e. two runs of
 // 8 adjacent columns.
 template <class E, bool kFull = false>
+__device__ inline void store_rows(E *Oh, long long row0, int rows_left, const f32x4 nt[4], f32x4 dt, int n16, int g);
+
+// bf16: token n's 16 values are two 16-byte pieces (x = 0, 1) of its 128-byte
+// row, one per lane group g.  Lanes n and n ^ 8 of each 16-lane row swap one
+// piece (DPP row rotate by 8), after which one store instruction covers rows
+// 0-7 of the tile and the other rows 8-15, each as whole 128-byte lines:
+// lane n < 8 writes (row n, x = 0) then (row n + 8, x = 0); lane n >= 8 writes
+// (row n - 8, x = 1) then (row n, x = 1).  Whole-line non-temporal writes
+// reach memory without partial-line overhead.
+template <class E, bool kFull>
 __device__ inline void store_rows(E *Oh, long long row0, int rows_left, const f32x4 nt[4], f32x4 dt, int n16, int g) {
   const float rd = __builtin_amdgcn_rcpf(dt[0]);
-  if (kFull || n16 < rows_left) {
-    E *row = Oh + (row0 + n16) * kD;
-    store_row8<E>(row, g, 0, nt[0] * rd, nt[1] * rd);
-    store_row8<E>(row, g, 1, nt[2] * rd, nt[3] * rd);
+  if constexpr (std::is_same<E, __bf16>::value) {
+    const f32x4 a0 = nt[0] * rd, a1 = nt[1] * rd, b0 = nt[2] * rd, b1 = nt[3] * rd;
+    const u32x4 p0 = {pack_bf16(a0[0], a0[1]), pack_bf16(a0[2], a0[3]), pack_bf16(a1[0], a1[1]), pack_bf16(a1[2], a1[3])};
+    const u32x4 p1 = {pack_bf16(b0[0], b0[1]), pack_bf16(b0[2], b0[3]), pack_bf16(b1[0], b1[1]), pack_bf16(b1[2], b1[3])};
+    const bool low = n16 < 8;
+    u32x4 send = low ? p1 : p0, recv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      recv[i] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send[i], 0x128 /* row_ror:8 */, 0xf, 0xf, false);
+    const u32x4 first = low ? p0 : recv, second = low ? recv : p1;
+    const int r_first = n16 & 7, x = n16 >> 3;
+    if (kFull || r_first < rows_left)
+      __builtin_nontemporal_store(first, reinterpret_cast<u32x4 *>(Oh + (row0 + r_first) * kD) + 4 * x + g);
+    if (kFull || r_first + 8 < rows_left)
+      __builtin_nontemporal_store(second, reinterpret_cast<u32x4 *>(Oh + (row0 + r_first + 8) * kD) + 4 * x + g);
+  } else {
+    if (kFull || n16 < rows_left) {
+      E *row = Oh + (row0 + n16) * kD;
+      store_row8<E>(row, g, 0, nt[0] * rd, nt[1] * rd);
+      store_row8<E>(row, g, 1, nt[2] * rd, nt[3] * rd);
+    }
   }
 }
 
