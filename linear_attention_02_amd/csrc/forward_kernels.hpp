@@ -162,19 +162,24 @@ template <> __device__ inline void phi_frag<float>(Frag<float> &f) {
 // ---------------------------------------------------------------------------
 // bf16 path: chunks staged in LDS.  The next chunk is fetched with
 // global_load_lds_dwordx4 (HBM -> LDS without passing through VGPRs) into a
-// wave-private slot while the current chunk is computed.  Lane l's 16 bytes
-// of load instruction i land at slot + 1024 i + 16 l; instruction (tsr, it, x)
-// carries rows 16it + n, columns 32x + 8g .. +7 of tensor tsr (n = l & 15,
-// g = l >> 4).  No other wave touches the slot, so no barrier is needed --
-// only the wave's own wait counters.
+// wave-private slot while the current chunk is computed.  Each load
+// instruction fetches 8 whole 128-byte rows: lane l loads row 8i + (l >> 3),
+// 16-byte piece p = (l & 7) ^ (row & 7), and its bytes land at
+// slot + 1024 i + 16 l.  So piece p of row R sits at 16-byte index
+// 64 (R >> 3) + 8 (R & 7) + (p ^ (R & 7)); the XOR spreads the transpose
+// reads below over the LDS banks.  No other wave touches the slot, so no
+// barrier is needed -- only the wave's own wait counters.
 //
-// Row layout fragments are the lane's own 16 bytes (ds_read_b128).  Token
-// layout fragments come from ds_read_b64_tr_b16, which within each group of
-// 16 lanes hands output lane i, register s, element i & 3 of the 8 bytes read
-// by lane 4s + (i >> 2).  Lane (src, g) therefore reads row 16jt + 4g +
-// (src >> 2), columns pi(mt, src & 3, 0..3), and lane (n, g) receives
-// X[16jt + 4g + r][pi(mt, n >> 2, n & 3)], the token layout above.
+// Row layout fragments: lane (n, g) reads pieces g and 4 + g of its row
+// (ds_read_b128 each).  Token layout fragments come from ds_read_b64_tr_b16,
+// which within each group of 16 lanes hands output lane i, register s,
+// element i & 3 of the 8 bytes read by lane 4s + (i >> 2).  Lane (src, g)
+// therefore reads row 16jt + 4g + (src >> 2), columns pi(mt, src & 3, 0..3),
+// and lane (n, g) receives X[16jt + 4g + r][pi(mt, n >> 2, n & 3)], the token
+// layout above.
 // ---------------------------------------------------------------------------
+__device__ inline int stage_index(int R, int p) { return 64 * (R >> 3) + 8 * (R & 7) + (p ^ (R & 7)); }
+
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short i16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
@@ -196,18 +201,17 @@ __device__ inline void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4
 template <int kTensors, int NT = 4>
 __device__ inline void stage_issue(u32x4 *slot, const __bf16 *const src[kTensors], long long t0, int rows, int n16,
                                    int g) {
+  const int lane = 16 * g + n16;
+  const int sub = lane >> 3;                 // row within the instruction's 8
+  const int piece = (lane & 7) ^ sub;        // (row & 7) == sub
 #pragma unroll
   for (int tsr = 0; tsr < kTensors; ++tsr) {
 #pragma unroll
-    for (int it = 0; it < NT; ++it) {
-      const int row = 16 * it + n16;
-      if (row < rows) {
-        const u32x4 *gp = reinterpret_cast<const u32x4 *>(src[tsr] + (t0 + row) * kD);
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-          __builtin_amdgcn_global_load_lds(gp + 4 * x + g, (lds_void *)(slot + ((tsr * NT + it) * 2 + x) * 64), 16,
-                                           0, 0);
-      }
+    for (int i = 0; i < 2 * NT; ++i) {
+      const int row = 8 * i + sub;
+      if (row < rows)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4 *>(src[tsr] + (t0 + row) * kD) + piece,
+                                         (lds_void *)(slot + (tsr * 2 * NT + i) * 64), 16, 0, 0);
     }
   }
 }
@@ -215,9 +219,10 @@ __device__ inline void stage_issue(u32x4 *slot, const __bf16 *const src[kTensors
 // Row layout fragments of tensor tsr, row tile it (raw, no phi).
 template <int NT = 4>
 __device__ inline void lds_row_frags(const u32x4 *slot, int tsr, int it, int lane, Frag<__bf16> f[4]) {
+  const int R = 16 * it + (lane & 15), g = lane >> 4;
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
-    const u32x4 v = slot[((tsr * NT + it) * 2 + x) * 64 + lane];
+    const u32x4 v = slot[tsr * 2 * NT * 64 + stage_index(R, 4 * x + g)];
     f[2 * x].w[0] = v[0];
     f[2 * x].w[1] = v[1];
     f[2 * x + 1].w[0] = v[2];
@@ -229,7 +234,8 @@ __device__ inline void lds_row_frags(const u32x4 *slot, int tsr, int it, int lan
 template <int NT = 4>
 __device__ inline Frag<__bf16> lds_tok_frag(const u32x4 *slot, int tsr, int jt, int mt, int lane) {
   const int src = lane & 15, g = lane >> 4;
-  const int byte = ((tsr * NT + jt) * 2 + (mt >> 1)) * 1024 + ((src & 3) * 16 + 4 * g + (src >> 2)) * 16 + 8 * (mt & 1);
+  const int R = 16 * jt + 4 * g + (src >> 2);
+  const int byte = (tsr * 2 * NT * 64 + stage_index(R, 4 * (mt >> 1) + (src & 3))) * 16 + 8 * (mt & 1);
   const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_i16x4 *)(reinterpret_cast<__attribute__((address_space(3))) char *>((lds_void *)slot) + byte));
   Frag<__bf16> f;
