@@ -69,8 +69,10 @@ struct TimerScope {
   TimerScope(const char *name, hipStream_t s) : stream(s) {
     if (!g_timer_on.load(std::memory_order_relaxed)) return;
     ev.name = name;
-    if (hipEventCreate(&ev.start) != hipSuccess) return;
-    if (hipEventCreate(&ev.stop) != hipSuccess) {
+    // No system-scope fence on recording: the events only timestamp the
+    // stream, and a fence per kernel boundary would itself cost microseconds.
+    if (hipEventCreateWithFlags(&ev.start, hipEventDisableSystemFence) != hipSuccess) return;
+    if (hipEventCreateWithFlags(&ev.stop, hipEventDisableSystemFence) != hipSuccess) {
       (void)hipEventDestroy(ev.start);
       return;
     }
