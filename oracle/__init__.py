@@ -14,6 +14,12 @@ Forms, each following a definition on the pages:
     z_i = z_{i-1} + phi(k_i), o_i = phi(q_i)^T S_i / phi(q_i)^T z_i (same page,
     §7.2), or with ``causal=False`` the reassociated non-causal form (§6.2).
   * ``decode_step`` -- one step of that recurrence on an fp64 state (§7.2).
+  * ``backward_quadratic`` / ``backward_recurrent`` -- dQ, dK, dV of O1 for a
+    given dL/dO, by the chain rule over every (i, j) pair, and as forward and
+    backward cumulative sums ("[Paper Review] Transformers are RNNs", §3.5,
+    states that form without printing it; the derivation is in oracle.c).
+    With ``companion=True`` they return elementwise bounds of the gradients'
+    magnitudes, the scale that parity errors are measured on.
 
 Element types accepted: float64, float32, and bfloat16 passed as its raw
 16-bit patterns in a uint16 array.
@@ -59,6 +65,13 @@ def lib() -> ctypes.CDLL:
         L.oracle_forward_recurrent.argtypes = [vp, vp, vp, ctypes.c_int, ctypes.c_long, ctypes.c_long,
                                                ctypes.c_long, ctypes.c_long, ctypes.c_int, ctypes.c_int,
                                                dp, dp, dp, dp, dp, ctypes.c_int]
+        for name in ("oracle_backward_quadratic", "oracle_backward_recurrent"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_long, ctypes.c_long, ctypes.c_long,
+                          ctypes.c_long, ctypes.c_int, ctypes.c_int, dp, dp, dp, ctypes.c_int]
+        L.oracle_phi_prime.restype = ctypes.c_double
+        L.oracle_phi_prime.argtypes = [ctypes.c_double]
         L.oracle_decode_step.restype = ctypes.c_int
         L.oracle_decode_step.argtypes = [dp, dp, vp, vp, vp, ctypes.c_int, ctypes.c_long, ctypes.c_long,
                                          ctypes.c_long, ctypes.c_int, dp, ctypes.c_int]
@@ -122,7 +135,7 @@ def _prep(*arrays: np.ndarray):
     out = [np.ascontiguousarray(a) for a in arrays]
     codes = {_dtype_code(a) for a in out}
     if len(codes) != 1:
-        raise OracleError("q, k and v must share one element type")
+        raise OracleError("q, k, v (and dO) must share one element type")
     return out, codes.pop()
 
 
@@ -205,6 +218,37 @@ def decode_step(S: np.ndarray, z: np.ndarray, q, k, v, absv: bool = False,
                                   U, C, M, int(bool(absv)), _dptr(o), threads or default_threads())
     _check(rc, "decode_step", allow_nonpositive)
     return o
+
+
+def phi_prime(x: float) -> float:
+    return lib().oracle_phi_prime(float(x))
+
+
+def _backward(fn_name: str, q, k, v, g, causal: bool, companion: bool, threads, allow_nonpositive):
+    (q, k, v, g), code = _prep(q, k, v, g)
+    B, H, N, C, M = _shape4(q, k, v)
+    if g.shape != v.shape:
+        raise OracleError(f"dO shape {g.shape} differs from V {v.shape}")
+    dq = np.empty((B, H, N, C), dtype=np.float64)
+    dk = np.empty((B, H, N, C), dtype=np.float64)
+    dv = np.empty((B, H, N, M), dtype=np.float64)
+    rc = getattr(lib(), fn_name)(q.ctypes.data, k.ctypes.data, v.ctypes.data, g.ctypes.data, code, B * H, N, C,
+                                 M, int(bool(causal)), int(bool(companion)), _dptr(dq), _dptr(dk), _dptr(dv),
+                                 threads or default_threads())
+    _check(rc, fn_name, allow_nonpositive)
+    return dq, dk, dv
+
+
+def backward_quadratic(q, k, v, g, causal: bool, companion: bool = False, threads: Optional[int] = None,
+                       allow_nonpositive: bool = False):
+    """dQ, dK, dV of O1 for dL/dO = g, by the definition (O(N^2)); or their magnitude companion."""
+    return _backward("oracle_backward_quadratic", q, k, v, g, causal, companion, threads, allow_nonpositive)
+
+
+def backward_recurrent(q, k, v, g, causal: bool, companion: bool = False, threads: Optional[int] = None,
+                       allow_nonpositive: bool = False):
+    """The same gradients (or companion) as forward and backward cumulative sums, O(N C M)."""
+    return _backward("oracle_backward_recurrent", q, k, v, g, causal, companion, threads, allow_nonpositive)
 
 
 def parity_error(out: np.ndarray, ref: np.ndarray, mag: np.ndarray) -> Tuple[float, dict]:
