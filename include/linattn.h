@@ -119,6 +119,37 @@ linattn_status linattn_forward_state(const void *Q, const void *K, const void *V
 /* Workspace for linattn_forward_state (the causal plan plus state staging). */
 size_t linattn_forward_state_workspace_bytes(int B, int H, int N, int C, int M, linattn_dtype dt);
 
+/* Bytes of device workspace `linattn_backward` needs (0 for invalid
+ * arguments, which `linattn_backward` reports). */
+size_t linattn_backward_workspace_bytes(int B, int H, int N, int C, int M, linattn_dtype dt, int causal);
+
+/*
+ * linattn_backward -- gradients of linattn_forward (zero initial state) with
+ * respect to Q, K and V for a given dL/dO, in time and memory linear in N:
+ * the gradients are themselves forward and reverse cumulative sums ("[Paper
+ * Review] Transformers are RNNs", §3.5 "Gradient Computation"; "Transformers
+ * Are RNNs: Linear Attention" knowledge note).  With g_i = dL/do_i,
+ * den_i = phi(q_i)^T z_i, a_i = g_i / den_i and b_i = -(g_i . o_i) / den_i:
+ *   dphi(q_i) = S_i a_i + b_i z_i            (S_i, z_i: prefix sums as in the forward)
+ *   dphi(k_j) = R_j v_j + r_j,  dv_j = R_j^T phi(k_j)
+ *   R_j = sum_{i: j in J(i)} phi(q_i) a_i^T,  r_j = sum_{i: j in J(i)} b_i phi(q_i)
+ *   dq = dphi(q) * phi'(q),  phi'(x) = 1 for x > 0, e^x otherwise.
+ * o_i is recomputed in fp32 (the forward's output is not an argument).
+ *
+ * Q, K, V, dO: [B,H,N,64] in `dt`; dQ, dK, dV: [B,H,N,64] in `dt`, written.
+ * causal as in linattn_forward.  Accumulation is fp32; bf16 outputs are
+ *   rounded to nearest-even.
+ * workspace: device buffer of at least linattn_backward_workspace_bytes(...)
+ *   bytes, 16-byte aligned; contents on entry do not matter.
+ * B == 0, H == 0 or N == 0: returns LINATTN_OK and enqueues nothing.
+ * Errors: NULL, SHAPE, DTYPE, ALIGN, ALIAS (an output overlaps an input, the
+ *   outputs overlap each other, or the workspace overlaps any of them),
+ *   WORKSPACE, HIP.  Deterministic like linattn_forward.
+ */
+linattn_status linattn_backward(const void *Q, const void *K, const void *V, const void *dO, void *dQ, void *dK,
+                                void *dV, int B, int H, int N, int C, int M, linattn_dtype dt, int causal,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
 /*
  * linattn_decode_step -- one constant-state recurrent step for BH independent
  * heads ("Why Replace Attention?", §7.2, steps 1-4; §7.4 constant work per

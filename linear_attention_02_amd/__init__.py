@@ -66,6 +66,10 @@ def lib() -> ctypes.CDLL:
         L.linattn_forward.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
         L.linattn_forward_state.restype = i
         L.linattn_forward_state.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]
+        L.linattn_backward_workspace_bytes.restype = sz
+        L.linattn_backward_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        L.linattn_backward.restype = i
+        L.linattn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
         L.linattn_decode_step.restype = i
         L.linattn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
         L.linattn_timer_enable.restype = None
@@ -204,6 +208,30 @@ def forward_state(q, k, v, S0=None, z0=None, out=None, S_out=None, z_out=None, w
                                      _ptr(S_out), _ptr(z_out), _ptr(ws), nbytes, _stream(stream))
     _raise(rc)
     return out, S_out, z_out
+
+
+def backward_workspace_bytes(B: int, H: int, N: int, dtype, causal: bool) -> int:
+    dt = F32 if str(dtype).endswith("float32") else BF16
+    return int(lib().linattn_backward_workspace_bytes(B, H, N, 64, 64, dt, int(bool(causal))))
+
+
+def backward(q, k, v, grad_out, causal: bool = True, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients of ``forward`` (zero initial state) for dL/dO = grad_out; returns (dq, dk, dv)."""
+    torch = _torch()
+    _check_cuda(q, k, v, grad_out, dq, dk, dv)
+    B, H, N, C, M = _shape(q, k, v)
+    if grad_out.shape != v.shape or grad_out.dtype != v.dtype:
+        raise LinattnError(2, "grad_out must match v in shape and dtype")
+    dt = _dt(q)
+    dq = torch.empty(q.shape, dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=k.dtype, device=k.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=v.dtype, device=v.device) if dv is None else dv
+    nbytes = int(lib().linattn_backward_workspace_bytes(B, H, N, C, M, dt, int(bool(causal))))
+    ws = _alloc_ws(nbytes, q.device, workspace)
+    rc = lib().linattn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(grad_out), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N,
+                                C, M, dt, int(bool(causal)), _ptr(ws), nbytes, _stream(stream))
+    _raise(rc)
+    return dq, dk, dv
 
 
 def decode_step(S, z, q, k, v, out=None, stream=None):

@@ -1,8 +1,8 @@
 // api.hip -- the C ABI of liblinattn.so (declared in include/linattn.h).
 //
 // Host side only: validate arguments, plan the launch, enqueue kernels on the
-// caller's stream.  All arithmetic runs in the kernels of forward_kernels.hpp
-// and decode_kernel.hpp.
+// caller's stream.  All arithmetic runs in the kernels of forward_kernels.hpp,
+// backward_kernels.hpp and decode_kernel.hpp.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "../../include/linattn.h"
+#include "backward_kernels.hpp"
 #include "decode_kernel.hpp"
 #include "forward_kernels.hpp"
 #include "validate.hpp"
@@ -117,7 +118,7 @@ linattn_status run_forward(const FwdParams &base, const Plan &plan, int causal, 
       if (launch_error("seg_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
       {
         TimerScope t("scan", stream);
-        hipLaunchKernelGGL(scan_kernel, dim3(scan_blocks), dim3(256), 0, stream, p, 1);
+        hipLaunchKernelGGL(scan_kernel, dim3(scan_blocks), dim3(256), 0, stream, p, kScanPrefix);
       }
       if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
       p.init = kInitRecord;
@@ -138,7 +139,7 @@ linattn_status run_forward(const FwdParams &base, const Plan &plan, int causal, 
     if (launch_error("seg_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
     {
       TimerScope t("scan", stream);
-      hipLaunchKernelGGL(scan_kernel, dim3(scan_blocks), dim3(256), 0, stream, p, 0);
+      hipLaunchKernelGGL(scan_kernel, dim3(scan_blocks), dim3(256), 0, stream, p, kScanTotal);
     }
     if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
     {
@@ -149,6 +150,131 @@ linattn_status run_forward(const FwdParams &base, const Plan &plan, int causal, 
     if (launch_error("noncausal_read") != LINATTN_OK) return LINATTN_ERR_HIP;
   }
   return set_status(LINATTN_OK, "");
+}
+
+template <class E>
+linattn_status run_backward(const BwdParams &base, const BwdPlan &bp, int causal, hipStream_t stream,
+                            linattn_dtype dt) {
+  const Plan &plan = bp.fwd;
+  BwdParams p = base;
+  p.segments = plan.segments;
+  p.seg_chunks = plan.seg_chunks;
+  p.ranges = plan.ranges;
+  p.range_chunks = plan.range_chunks;
+  p.recF = plan.records;
+  p.recR = bp.recR;
+  // The forward's totals and scan kernels produce the (S, z) records.
+  FwdParams f{};
+  f.Q = p.Q;
+  f.K = p.K;
+  f.V = p.V;
+  f.N = p.N;
+  f.heads = p.heads;
+  f.segments = plan.segments;
+  f.seg_chunks = plan.seg_chunks;
+  f.ws = p.wsF;
+  f.records = plan.records;
+  FwdParams r = f;  // the scan over the (R, r) records
+  r.ws = p.wsR;
+  r.records = bp.recR;
+  const unsigned heads = (unsigned)plan.heads;
+  const unsigned scan_blocks = (unsigned)((plan.heads * kStateFloats + 255) / 256);
+  const unsigned P = (unsigned)plan.segments;
+  if (causal) {
+    if (P > 1) {
+      {
+        TimerScope t(kname("seg_totals", dt), stream);
+        hipLaunchKernelGGL(seg_totals_kernel<E>, dim3(heads * (P - 1)), dim3(64), 0, stream, f, (int)P - 1);
+      }
+      if (launch_error("seg_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
+      {
+        TimerScope t("scan", stream);
+        hipLaunchKernelGGL(scan_kernel, dim3(scan_blocks), dim3(256), 0, stream, f, kScanPrefix);
+      }
+      if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
+    }
+    {
+      TimerScope t(kname("bwd_walk_f", dt), stream);
+      hipLaunchKernelGGL(BwdKernels<E>::walk_f, dim3(heads * P), dim3(64), 0, stream, p);
+    }
+    if (launch_error("bwd_walk_f") != LINATTN_OK) return LINATTN_ERR_HIP;
+    if (P > 1) {
+      {
+        TimerScope t(kname("bwd_reverse_totals", dt), stream);
+        hipLaunchKernelGGL(BwdKernels<E>::reverse_totals, dim3(heads * (P - 1)), dim3(64), 0, stream, p);
+      }
+      if (launch_error("bwd_reverse_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
+      {
+        TimerScope t("scan", stream);
+        hipLaunchKernelGGL(scan_kernel, dim3(scan_blocks), dim3(256), 0, stream, r, kScanSuffix);
+      }
+      if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
+    }
+    {
+      TimerScope t(kname("bwd_walk_r", dt), stream);
+      hipLaunchKernelGGL(BwdKernels<E>::walk_r, dim3(heads * P), dim3(64), 0, stream, p);
+    }
+    if (launch_error("bwd_walk_r") != LINATTN_OK) return LINATTN_ERR_HIP;
+  } else {
+    {
+      TimerScope t(kname("seg_totals", dt), stream);
+      hipLaunchKernelGGL(seg_totals_kernel<E>, dim3(heads * P), dim3(64), 0, stream, f, (int)P);
+    }
+    if (launch_error("seg_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
+    {
+      TimerScope t("scan", stream);
+      hipLaunchKernelGGL(scan_kernel, dim3(scan_blocks), dim3(256), 0, stream, f, kScanTotal);
+    }
+    if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
+    {
+      TimerScope t(kname("bwd_nc_a", dt), stream);
+      hipLaunchKernelGGL(BwdKernels<E>::nc_a, dim3(heads * (unsigned)plan.ranges), dim3(64), 0, stream, p);
+    }
+    if (launch_error("bwd_nc_a") != LINATTN_OK) return LINATTN_ERR_HIP;
+    r.segments = plan.ranges;
+    {
+      TimerScope t("scan", stream);
+      hipLaunchKernelGGL(scan_kernel, dim3(scan_blocks), dim3(256), 0, stream, r, kScanTotal);
+    }
+    if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
+    {
+      TimerScope t(kname("bwd_nc_b", dt), stream);
+      hipLaunchKernelGGL(BwdKernels<E>::nc_b, dim3(heads * (unsigned)plan.ranges), dim3(64), 0, stream, p);
+    }
+    if (launch_error("bwd_nc_b") != LINATTN_OK) return LINATTN_ERR_HIP;
+  }
+  return set_status(LINATTN_OK, "");
+}
+
+linattn_status backward_impl(const void *Q, const void *K, const void *V, const void *dO, void *dQ, void *dK,
+                             void *dV, int B, int H, int N, int C, int M, linattn_dtype dt, int causal,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+  const long long heads = (long long)B * (long long)H;
+  BwdPlan bp;
+  if (B >= 0 && H >= 0 && N >= 0)
+    bp = plan_backward(heads, N, causal, (heads > 0 && N > 0) ? compute_units() : 1, g_segment_override.load());
+  const Check c = check_backward(Q, K, V, dO, dQ, dK, dV, B, H, N, C, M, dt, workspace, workspace_bytes,
+                                 (heads > 0 && N > 0) ? bp.workspace_bytes : 0);
+  if (!c.ok()) return from_check(c);
+  if (heads == 0 || N == 0) return set_status(LINATTN_OK, "");
+  BwdParams p{};
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.dO = dO;
+  p.dQ = dQ;
+  p.dK = dK;
+  p.dV = dV;
+  p.N = N;
+  p.heads = (int)heads;
+  char *ws = reinterpret_cast<char *>(workspace);
+  p.wsF = reinterpret_cast<float *>(ws);
+  p.wsR = reinterpret_cast<float *>(ws + bp.off_r);
+  p.stats = reinterpret_cast<f32x2 *>(ws + bp.off_stats);
+  p.stats_stride = bp.stats_stride;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dt == LINATTN_BF16) return run_backward<__bf16>(p, bp, causal, s, dt);
+  return run_backward<float>(p, bp, causal, s, dt);
 }
 
 // Writes S_out/z_out = S0/z0 (or zero) for every head: the N == 0 case of
@@ -249,6 +375,23 @@ linattn_status linattn_forward_state(const void *Q, const void *K, const void *V
                                      float *z_out, void *workspace, size_t workspace_bytes, void *stream) {
   try {
     return forward_impl(Q, K, V, O, B, H, N, C, M, dt, 1, S0, z0, S_out, z_out, workspace, workspace_bytes, stream);
+  } catch (...) {
+    return set_status(LINATTN_ERR_ARG, "internal exception");
+  }
+}
+
+size_t linattn_backward_workspace_bytes(int B, int H, int N, int C, int M, linattn_dtype dt, int causal) {
+  if (B <= 0 || H <= 0 || N <= 0 || C != 64 || M != 64 || dtype_bytes(dt) == 0) return 0;
+  const BwdPlan p = plan_backward((long long)B * H, N, causal, compute_units(), g_segment_override.load());
+  return p.workspace_bytes == SIZE_MAX ? 0 : p.workspace_bytes;
+}
+
+linattn_status linattn_backward(const void *Q, const void *K, const void *V, const void *dO, void *dQ, void *dK,
+                                void *dV, int B, int H, int N, int C, int M, linattn_dtype dt, int causal,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+  try {
+    return backward_impl(Q, K, V, dO, dQ, dK, dV, B, H, N, C, M, dt, causal ? 1 : 0, workspace, workspace_bytes,
+                         stream);
   } catch (...) {
     return set_status(LINATTN_ERR_ARG, "internal exception");
   }

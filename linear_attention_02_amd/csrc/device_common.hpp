@@ -73,20 +73,23 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
 template <class E> struct Frag;
 
 template <> struct Frag<__bf16> {
-  uint32_t w[2];  // element r lives in half (r & 1) of w[r >> 1]
+  // Element r lives in half (r & 1) of w[r >> 1].  A vector rather than an
+  // array, so that fragments stored in arrays are always accessed as whole
+  // values and stay in registers.
+  u32x2 w;
 };
 template <> struct Frag<float> {
   float v[4];
 };
 
 template <class E> __device__ inline Frag<E> frag_zero();
-template <> __device__ inline Frag<__bf16> frag_zero<__bf16>() { return {{0u, 0u}}; }
+template <> __device__ inline Frag<__bf16> frag_zero<__bf16>() { return {u32x2{0u, 0u}}; }
 template <> __device__ inline Frag<float> frag_zero<float>() { return {{0.f, 0.f, 0.f, 0.f}}; }
 
 // Accumulator (fp32) -> operand fragment.
 template <class E> __device__ inline Frag<E> to_frag(f32x4 a);
 template <> __device__ inline Frag<__bf16> to_frag<__bf16>(f32x4 a) {
-  return {{pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3])}};
+  return {u32x2{pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3])}};
 }
 template <> __device__ inline Frag<float> to_frag<float>(f32x4 a) { return {{a[0], a[1], a[2], a[3]}}; }
 
@@ -105,7 +108,7 @@ template <> __device__ inline Frag<float> frag_identity<float>(int n16, int g) {
   return {{d == 0 ? 1.f : 0.f, d == 1 ? 1.f : 0.f, d == 2 ? 1.f : 0.f, d == 3 ? 1.f : 0.f}};
 }
 template <class E> __device__ inline Frag<E> frag_ones();
-template <> __device__ inline Frag<__bf16> frag_ones<__bf16>() { return {{0x3f803f80u, 0x3f803f80u}}; }
+template <> __device__ inline Frag<__bf16> frag_ones<__bf16>() { return {u32x2{0x3f803f80u, 0x3f803f80u}}; }
 template <> __device__ inline Frag<float> frag_ones<float>() { return {{1.f, 1.f, 1.f, 1.f}}; }
 
 // ---------------------------------------------------------------------------
@@ -118,14 +121,14 @@ template <> __device__ inline Frag<float> frag_ones<float>() { return {{1.f, 1.f
 // ---------------------------------------------------------------------------
 __device__ inline f32x4 mma2_bf16(f32x4 acc, const Frag<__bf16> &a0, const Frag<__bf16> &a1,
                                   const Frag<__bf16> &b0, const Frag<__bf16> &b1) {
-  const u32x4 a = {a0.w[0], a0.w[1], a1.w[0], a1.w[1]};
-  const u32x4 b = {b0.w[0], b0.w[1], b1.w[0], b1.w[1]};
+  const u32x4 a = __builtin_shufflevector(a0.w, a1.w, 0, 1, 2, 3);
+  const u32x4 b = __builtin_shufflevector(b0.w, b1.w, 0, 1, 2, 3);
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc,
                                                  0, 0, 0);
 }
 __device__ inline f32x4 mma1_bf16(f32x4 acc, const Frag<__bf16> &a, const Frag<__bf16> &b) {
-  const u32x2 av = {a.w[0], a.w[1]};
-  const u32x2 bv = {b.w[0], b.w[1]};
+  const u32x2 av = a.w;
+  const u32x2 bv = b.w;
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av), __builtin_bit_cast(i16x4, bv), acc,
                                                    0, 0, 0);
 }

@@ -350,12 +350,10 @@ __device__ inline void state_read(const StateOperands<E> &so, const Frag<E> qf[4
   dt = mac2<E>(dt, z2, z3, q2, q3);
 }
 
-// o = num / den for 16 tokens and store: lane (n, g) holds token n's value
+// Store four accumulator tiles of 16 tokens: lane (n, g) holds token n's
 // columns pi(mt, g, r) = 32x + 8g + 4y + r for mt = 2x + y, i.e. two runs of
 // 8 adjacent columns.
-template <class E, bool kFull = false>
-__device__ inline void store_rows(E *Oh, long long row0, int rows_left, const f32x4 nt[4], f32x4 dt, int n16, int g);
-
+//
 // bf16: token n's 16 values are two 16-byte pieces (x = 0, 1) of its 128-byte
 // row, one per lane group g.  Lanes n and n ^ 8 of each 16-lane row swap one
 // piece (DPP row rotate by 8), after which one store instruction covers rows
@@ -364,12 +362,12 @@ __device__ inline void store_rows(E *Oh, long long row0, int rows_left, const f3
 // (row n - 8, x = 1) then (row n, x = 1).  Whole-line non-temporal writes
 // reach memory without partial-line overhead.
 template <class E, bool kFull>
-__device__ inline void store_rows(E *Oh, long long row0, int rows_left, const f32x4 nt[4], f32x4 dt, int n16, int g) {
-  const float rd = __builtin_amdgcn_rcpf(dt[0]);
+__device__ inline void store_tiles(E *base, long long row0, int rows_left, const f32x4 a[4], int n16, int g) {
   if constexpr (std::is_same<E, __bf16>::value) {
-    const f32x4 a0 = nt[0] * rd, a1 = nt[1] * rd, b0 = nt[2] * rd, b1 = nt[3] * rd;
-    const u32x4 p0 = {pack_bf16(a0[0], a0[1]), pack_bf16(a0[2], a0[3]), pack_bf16(a1[0], a1[1]), pack_bf16(a1[2], a1[3])};
-    const u32x4 p1 = {pack_bf16(b0[0], b0[1]), pack_bf16(b0[2], b0[3]), pack_bf16(b1[0], b1[1]), pack_bf16(b1[2], b1[3])};
+    const u32x4 p0 = {pack_bf16(a[0][0], a[0][1]), pack_bf16(a[0][2], a[0][3]), pack_bf16(a[1][0], a[1][1]),
+                      pack_bf16(a[1][2], a[1][3])};
+    const u32x4 p1 = {pack_bf16(a[2][0], a[2][1]), pack_bf16(a[2][2], a[2][3]), pack_bf16(a[3][0], a[3][1]),
+                      pack_bf16(a[3][2], a[3][3])};
     const bool low = n16 < 8;
     u32x4 send = low ? p1 : p0, recv;
 #pragma unroll
@@ -378,16 +376,25 @@ __device__ inline void store_rows(E *Oh, long long row0, int rows_left, const f3
     const u32x4 first = low ? p0 : recv, second = low ? recv : p1;
     const int r_first = n16 & 7, x = n16 >> 3;
     if (kFull || r_first < rows_left)
-      __builtin_nontemporal_store(first, reinterpret_cast<u32x4 *>(Oh + (row0 + r_first) * kD) + 4 * x + g);
+      __builtin_nontemporal_store(first, reinterpret_cast<u32x4 *>(base + (row0 + r_first) * kD) + 4 * x + g);
     if (kFull || r_first + 8 < rows_left)
-      __builtin_nontemporal_store(second, reinterpret_cast<u32x4 *>(Oh + (row0 + r_first + 8) * kD) + 4 * x + g);
+      __builtin_nontemporal_store(second, reinterpret_cast<u32x4 *>(base + (row0 + r_first + 8) * kD) + 4 * x + g);
   } else {
     if (kFull || n16 < rows_left) {
-      E *row = Oh + (row0 + n16) * kD;
-      store_row8<E>(row, g, 0, nt[0] * rd, nt[1] * rd);
-      store_row8<E>(row, g, 1, nt[2] * rd, nt[3] * rd);
+      E *row = base + (row0 + n16) * kD;
+      store_row8<E>(row, g, 0, a[0], a[1]);
+      store_row8<E>(row, g, 1, a[2], a[3]);
     }
   }
+}
+
+// o = num / den for 16 tokens (num^T tiles nt, den in every register of dt),
+// stored as above.
+template <class E, bool kFull = false>
+__device__ inline void store_rows(E *Oh, long long row0, int rows_left, const f32x4 nt[4], f32x4 dt, int n16, int g) {
+  const float rd = __builtin_amdgcn_rcpf(dt[0]);
+  const f32x4 a[4] = {nt[0] * rd, nt[1] * rd, nt[2] * rd, nt[3] * rd};
+  store_tiles<E, kFull>(Oh, row0, rows_left, a, n16, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -470,6 +477,9 @@ __global__ __launch_bounds__(64, 1) void seg_totals_kernel(FwdParams p, int tota
 //   causal:     records 0..P-2 hold totals -> become exclusive prefixes seeded
 //               with S0/z0 (or zero); record P-1 receives the prefix of the
 //               last segment.
+//   reverse:    the same over the records in the opposite order: records
+//               P-1..1 hold totals and become exclusive suffix sums (sums over
+//               the later segments); record 0 receives the suffix of segment 0.
 //   non-causal: record P receives the sum of records 0..P-1.
 // The loads do not depend on the running sum, so they are issued in batches
 // (one memory latency per batch) before the dependent stores.  The order of
@@ -477,16 +487,21 @@ __global__ __launch_bounds__(64, 1) void seg_totals_kernel(FwdParams p, int tota
 // ---------------------------------------------------------------------------
 constexpr int kScanBatch = 32;
 
-__global__ __launch_bounds__(256) void scan_kernel(FwdParams p, int causal) {
+enum ScanMode : int { kScanTotal = 0, kScanPrefix = 1, kScanSuffix = 2 };
+
+__global__ __launch_bounds__(256) void scan_kernel(FwdParams p, int mode) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const int h = (int)(idx / kStateFloats);
   const int e = (int)(idx % kStateFloats);
   if (h >= p.heads) return;
-  float *recs = p.ws + (long long)h * p.records * kStateFloats + e;
   const int P = p.segments;
-  if (causal) {
+  // Logical record s lives at position s (prefix) or P - 1 - s (suffix).
+  const long long step = mode == kScanSuffix ? -(long long)kStateFloats : (long long)kStateFloats;
+  float *recs = p.ws + (long long)h * p.records * kStateFloats + e +
+                (mode == kScanSuffix ? (long long)(P - 1) * kStateFloats : 0);
+  if (mode != kScanTotal) {
     float run = 0.f;
-    if (p.S0 != nullptr) {
+    if (mode == kScanPrefix && p.S0 != nullptr) {
       if (e < 4096) {
         const int ct = e >> 10, mt = (e >> 8) & 3, lane = (e >> 2) & 63, r = e & 3;
         const int c = pi_col(ct, lane >> 4, r);
@@ -502,15 +517,15 @@ __global__ __launch_bounds__(256) void scan_kernel(FwdParams p, int causal) {
       float t[kScanBatch];
 #pragma unroll
       for (int u = 0; u < kScanBatch; ++u)
-        if (s0 + u + 1 < P) t[u] = recs[(long long)(s0 + u) * kStateFloats];
+        if (s0 + u + 1 < P) t[u] = recs[(long long)(s0 + u) * step];
 #pragma unroll
       for (int u = 0; u < kScanBatch; ++u)
         if (s0 + u + 1 < P) {
-          recs[(long long)(s0 + u) * kStateFloats] = run;
+          recs[(long long)(s0 + u) * step] = run;
           run += t[u];
         }
     }
-    recs[(long long)(P - 1) * kStateFloats] = run;
+    recs[(long long)(P - 1) * step] = run;
   } else {
     float run = 0.f;
     for (int s0 = 0; s0 < P; s0 += kScanBatch) {

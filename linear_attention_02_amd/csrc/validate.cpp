@@ -90,6 +90,69 @@ Plan plan_forward(long long heads, long long N, int causal, int cus, int overrid
   return p;
 }
 
+namespace {
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+}  // namespace
+
+BwdPlan plan_backward(long long heads, long long N, int causal, int cus, int override_segments) {
+  BwdPlan b;
+  b.fwd = plan_forward(heads, N, causal, cus, override_segments);
+  if (heads <= 0 || N <= 0) return b;
+  const Plan &p = b.fwd;
+  b.recR = causal ? (p.segments > 1 ? p.segments : 0) : p.ranges + 1;
+  b.stats_stride = ceil_div(N, kChunkTokens) * kChunkTokens;
+  size_t f_bytes = p.workspace_bytes, r_bytes = 0, s_bytes = 0;
+  if (f_bytes == SIZE_MAX || !mul3((size_t)heads, (size_t)b.recR, kStateBytes, &r_bytes) ||
+      !mul3((size_t)heads, (size_t)b.stats_stride, 8, &s_bytes) || f_bytes > SIZE_MAX / 4 ||
+      r_bytes > SIZE_MAX / 4 || s_bytes > SIZE_MAX / 4) {
+    b.workspace_bytes = SIZE_MAX;
+    return b;
+  }
+  b.off_r = align256(f_bytes);
+  b.off_stats = align256(b.off_r + r_bytes);
+  b.workspace_bytes = b.off_stats + s_bytes;
+  return b;
+}
+
+Check check_backward(const void *Q, const void *K, const void *V, const void *dO, const void *dQ, const void *dK,
+                     const void *dV, int B, int H, int N, int C, int M, linattn_dtype dt, const void *workspace,
+                     size_t workspace_bytes, size_t workspace_needed) {
+  const size_t eb = dtype_bytes(dt);
+  if (eb == 0) return fail(LINATTN_ERR_DTYPE, "unknown element type");
+  if (B < 0 || H < 0 || N < 0) return fail(LINATTN_ERR_SHAPE, "B, H and N must be non-negative");
+  if (C != 64 || M != 64) return fail(LINATTN_ERR_SHAPE, "only C = M = 64 is supported");
+  if ((long long)B * (long long)H > INT_MAX) return fail(LINATTN_ERR_SHAPE, "B * H exceeds INT_MAX");
+  size_t elems = 0;
+  if (!mul3((size_t)B * (size_t)H, (size_t)N, 64, &elems) || elems > SIZE_MAX / eb)
+    return fail(LINATTN_ERR_SHAPE, "tensor size overflows");
+  if (elems == 0) return Check();
+  if (!Q || !K || !V || !dO || !dQ || !dK || !dV)
+    return fail(LINATTN_ERR_NULL, "Q, K, V, dO, dQ, dK and dV must be non-NULL");
+  for (const void *ptr : {Q, K, V, dO, dQ, dK, dV})
+    if (!aligned16(ptr)) return fail(LINATTN_ERR_ALIGN, "Q, K, V, dO, dQ, dK and dV must be 16-byte aligned");
+  const size_t bytes = elems * eb;
+  const Buffer in[] = {{Q, bytes, "Q"}, {K, bytes, "K"}, {V, bytes, "V"}, {dO, bytes, "dO"}};
+  const Buffer out[] = {{dQ, bytes, "dQ"}, {dK, bytes, "dK"}, {dV, bytes, "dV"}};
+  for (const Buffer &o : out)
+    for (const Buffer &i : in)
+      if (overlaps(o, i)) return fail(LINATTN_ERR_ALIAS, std::string(o.name) + " overlaps " + i.name);
+  if (overlaps(out[0], out[1]) || overlaps(out[0], out[2]) || overlaps(out[1], out[2]))
+    return fail(LINATTN_ERR_ALIAS, "dQ, dK and dV must not overlap");
+  if (workspace_needed > 0) {
+    if (workspace_needed == SIZE_MAX) return fail(LINATTN_ERR_SHAPE, "workspace size overflows");
+    if (workspace == nullptr || workspace_bytes < workspace_needed)
+      return fail(LINATTN_ERR_WORKSPACE, "workspace needs " + std::to_string(workspace_needed) + " bytes, got " +
+                                             std::to_string(workspace ? workspace_bytes : 0));
+    if (!aligned16(workspace)) return fail(LINATTN_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const Buffer bw{workspace, workspace_needed, "workspace"};
+    for (const Buffer &b : in)
+      if (overlaps(bw, b)) return fail(LINATTN_ERR_ALIAS, std::string("workspace overlaps ") + b.name);
+    for (const Buffer &b : out)
+      if (overlaps(bw, b)) return fail(LINATTN_ERR_ALIAS, std::string("workspace overlaps ") + b.name);
+  }
+  return Check();
+}
+
 Check check_forward(const void *Q, const void *K, const void *V, const void *O, int B, int H, int N, int C, int M,
                     linattn_dtype dt, const void *workspace, size_t workspace_bytes, size_t workspace_needed) {
   const size_t eb = dtype_bytes(dt);

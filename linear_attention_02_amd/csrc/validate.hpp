@@ -46,6 +46,25 @@ Plan plan_forward(long long heads, long long N, int causal, int cus, int overrid
 Check check_forward(const void *Q, const void *K, const void *V, const void *O, int B, int H, int N, int C, int M,
                     linattn_dtype dt, const void *workspace, size_t workspace_bytes, size_t workspace_needed);
 
+// Launch plan for one backward call: the forward plan's segments and ranges,
+// plus the workspace layout [records of (S, z)] [records of (R, r)] [per-token
+// pairs (1/den, b)], each region 256-byte aligned.
+struct BwdPlan {
+  Plan fwd;
+  int recR = 0;                  // reverse-direction records per head
+  long long stats_stride = 0;    // pairs per head (N rounded up to 64)
+  size_t off_r = 0;              // byte offset of the reverse records
+  size_t off_stats = 0;          // byte offset of the pairs
+  size_t workspace_bytes = 0;
+};
+
+BwdPlan plan_backward(long long heads, long long N, int causal, int cus, int override_segments);
+
+// Q, K, V, dO inputs and dQ, dK, dV outputs, all [B,H,N,64] in `dt`.
+Check check_backward(const void *Q, const void *K, const void *V, const void *dO, const void *dQ, const void *dK,
+                     const void *dV, int B, int H, int N, int C, int M, linattn_dtype dt, const void *workspace,
+                     size_t workspace_bytes, size_t workspace_needed);
+
 Check check_state_args(const float *S0, const float *z0, const float *S_out, const float *z_out, int B, int H,
                        const void *Q, const void *K, const void *V, const void *O, size_t qk_bytes,
                        size_t vo_bytes, const void *workspace, size_t workspace_bytes);

@@ -120,6 +120,45 @@ def test_planner_segments(L):
     assert L.linattn_forward_workspace_bytes(1, 1, 64, 64, 64, 1, 0) == 2 * 4160 * 4
 
 
+def _bwd(L, Q=0x100000, K=0x200000, V=0x300000, G=0x400000, dQ=0x500000, dK=0x600000, dV=0x700000, B=1, H=1,
+         N=64, C=64, M=64, dt=1, causal=1, ws=None, wsb=0):
+    return L.linattn_backward(Q, K, V, G, dQ, dK, dV, B, H, N, C, M, dt, causal, ws, wsb, None)
+
+
+def test_backward_rejects_bad_arguments(L):
+    assert _bwd(L, G=None) == NULL
+    assert _bwd(L, dV=None) == NULL
+    assert _bwd(L, C=32) == SHAPE
+    assert _bwd(L, N=-5) == SHAPE
+    assert _bwd(L, dt=9) == DTYPE
+    assert _bwd(L, dK=0x600008) == ALIGN
+    assert _bwd(L, dQ=0x100000 + 4096) == ALIAS   # dQ inside Q (8 KiB tensors)
+    assert _bwd(L, dK=0x400000) == ALIAS          # dK is dO
+    assert _bwd(L, dV=0x500000 + 4096) == ALIAS   # dV inside dQ
+    assert "overlap" in L.linattn_last_error().decode()
+    for B, H, N in ((0, 8, 100), (2, 0, 100), (2, 8, 0)):
+        assert L.linattn_backward(None, None, None, None, None, None, None, B, H, N, 64, 64, 1, 1, None, 0,
+                                  None) == OK
+
+
+def test_backward_workspace_rules(L):
+    # One head of 2^16 tokens: several segments, so both record sets and the
+    # per-token pairs are needed.
+    N = 1 << 16
+    need = L.linattn_backward_workspace_bytes(1, 1, N, 64, 64, 1, 1)
+    P = L.linattn_plan_segments(1, 1, N, 1, 1)
+    assert P > 1
+    assert need >= 2 * P * 4160 * 4 + N * 8
+    # A single-chunk causal head still needs the pairs.
+    assert L.linattn_backward_workspace_bytes(1, 1, 64, 64, 64, 1, 1) == 64 * 8
+    big = 1 << 30
+    args = dict(Q=big, K=2 * big, V=3 * big, G=4 * big, dQ=5 * big, dK=6 * big, dV=7 * big, N=N)
+    assert _bwd(L, **args) == WORKSPACE
+    assert _bwd(L, ws=8 * big, wsb=need - 1, **args) == WORKSPACE
+    assert _bwd(L, ws=6 * big + 4096, wsb=need, **args) == ALIAS   # workspace inside dK
+    assert _bwd(L, ws=8 * big + 8, wsb=need, **args) == ALIGN
+
+
 def test_timer_without_launches(L):
     la.timer.reset()
     assert la.timer.names() == []

@@ -129,3 +129,20 @@ def to_oracle_array(t: torch.Tensor):
     if t.dtype in (torch.float32, torch.float64):
         return t.numpy()
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def grad_output_seed(seed: int) -> int:
+    return int(seed) * 1_000_000 + 999_999
+
+
+def draw_grad_output(B: int, H: int, N: int, M: int, dtype: str, seed: int) -> torch.Tensor:
+    """dL/dO [B,H,N,M] for the gradient workloads: N(0, 1) from its own seed."""
+    g = torch.Generator("cpu").manual_seed(grad_output_seed(seed))
+    x = torch.randn((B, H, N, M), dtype=torch.float32, generator=g)
+    return x.to(DTYPES[dtype]).contiguous()
+
+
+def backward_inputs(w: ForwardWorkload):
+    """Q, K, V of the forward workload plus a dL/dO of V's shape."""
+    q, k, v = forward_inputs(w)
+    return q, k, v, draw_grad_output(w.B, w.H, w.N, w.M, w.dtype, w.seed)
