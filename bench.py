@@ -11,6 +11,8 @@ inputs resident in HBM.  The same run also times
   * the recurrent decode step on 256 sequences x 8 heads for 3072 steps
     (captured in one HIP graph, one kernel per step),
   * the non-causal forward on B=8, H=8, N=4096,
+  * the backward (dQ, dK, dV) of the headline and CIFAR-shaped workloads,
+  * forward and forward+backward time and peak memory for N = 2^9..2^16,
   * the fp64 CPU oracle on a bounded sample of the headline workload
     (`cpu_baseline`, rank 0 only).
 `roofline` is for the dominant kernel (the causal walk): algorithmic bytes
@@ -74,6 +76,8 @@ def parse_args():
     ap.add_argument("--decode-steps", type=int, default=None, help="default: the workload's 3072")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-noncausal", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens per head of the headline workload the oracle runs on (0 = all)")
@@ -124,6 +128,124 @@ def time_forward(la, torch, w, steps, warmup, segments, host_inputs=None):
         kernels[name] = {"avg_us": 1000.0 * kms / max(n, 1), "launches": n}
     del q, k, v, out, ws
     return ms, kernels, ms_events
+
+
+def time_backward(la, torch, w, steps, warmup):
+    """Times `steps` backward calls like time_forward: plainly, then with the
+    library's per-kernel events."""
+    from workloads import backward_inputs
+    q, k, v, g = (t.cuda() for t in backward_inputs(w))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = la.backward_workspace_bytes(w.B, w.H, w.N, q.dtype, w.causal)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        la.backward(q, k, v, g, causal=w.causal, dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream)
+
+    def timed(with_kernel_events: bool) -> float:
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        la.timer.reset()
+        la.timer.enable(with_kernel_events)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(steps):
+            call()
+        end.record(stream)
+        torch.cuda.synchronize()
+        la.timer.enable(False)
+        return start.elapsed_time(end) / steps
+
+    ms = timed(False)
+    ms_events = timed(True)
+    kernels = {}
+    for name in la.timer.names():
+        kms, n = la.timer.read(name)
+        kernels[name] = {"avg_us": 1000.0 * kms / max(n, 1), "launches": n}
+    del q, k, v, g, dq, dk, dv, ws
+    return ms, kernels, ms_events
+
+
+def backward_record(la, torch, w, steps, warmup):
+    ms, kernels, ms_events = time_backward(la, torch, w, steps, warmup)
+    eb = 2 if w.dtype == "bf16" else 4
+    head_tokens = w.B * w.H * w.N
+    row = 64 * eb
+    alg = head_tokens * 7 * row  # read Q, K, V, dO; write dQ, dK, dV
+    rec = {"workload": w.name, "ms": ms, "ms_with_kernel_events": ms_events,
+           "tokens_per_s": w.tokens / (ms / 1000.0), "algorithmic_bytes": alg,
+           "achieved_GBs": alg / (ms * 1e-3) / 1e9, "frac_hbm": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "kernels": kernels}
+    # Per-kernel rooflines on the bytes each kernel must move in this design:
+    # walk_f reads Q, K, V, dO and writes dQ and one 8-byte pair per token;
+    # walk_r reads Q, K, V, dO and the pairs and writes dK, dV.
+    per_token = {f"bwd_walk_f_{w.dtype}": 5 * row + 8, f"bwd_walk_r_{w.dtype}": 6 * row + 8,
+                 f"bwd_nc_a_{w.dtype}": 3 * row + 8, f"bwd_nc_b_{w.dtype}": 4 * row}
+    roof = {}
+    for name, b in per_token.items():
+        if name in kernels:
+            us = kernels[name]["avg_us"]
+            gbs = head_tokens * b / (us * 1e-6) / 1e9
+            roof[name] = {"bytes_per_launch": head_tokens * b, "avg_launch_us": us, "achieved_GBs": gbs,
+                          "frac_hbm": gbs / HBM_PEAK_GBS}
+    rec["kernel_rooflines"] = roof
+    return rec
+
+
+def sequence_sweep(la, torch, steps, warmup, B=1, H=8, exps=range(9, 17)):
+    """Forward and forward+backward time and peak device memory against N
+    (causal, bf16, B=1, H=8, C=M=64): the pages' memory/time sweep over
+    sequence lengths 2^9..2^16, for this library's attention alone."""
+    from workloads import draw_grad_output, draw_qkv
+    rows = []
+    for e in exps:
+        N = 1 << e
+        q, k, v = (t.cuda() for t in draw_qkv(B, H, N, 64, 64, "bf16", seed=4000 + e))
+        g = draw_grad_output(B, H, N, 64, "bf16", 4000 + e).cuda()
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        o = la.forward(q, k, v, causal=True)
+        grads = la.backward(q, k, v, g, causal=True)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        del o, grads
+        fwd_ws = torch.empty(max(la.workspace_bytes(B, H, N, torch.bfloat16, True), 1), dtype=torch.uint8,
+                             device="cuda")
+        bwd_ws = torch.empty(max(la.backward_workspace_bytes(B, H, N, torch.bfloat16, True), 1),
+                             dtype=torch.uint8, device="cuda")
+        o = torch.empty_like(v)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+        def fwd():
+            la.forward(q, k, v, causal=True, out=o, workspace=fwd_ws)
+
+        def fwd_bwd():
+            fwd()
+            la.backward(q, k, v, g, causal=True, dq=dq, dk=dk, dv=dv, workspace=bwd_ws)
+
+        res = {"N": N}
+        for key, fn in (("fwd_ms", fwd), ("fwd_bwd_ms", fwd_bwd)):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            start.record()
+            for _ in range(steps):
+                fn()
+            end.record()
+            torch.cuda.synchronize()
+            res[key] = start.elapsed_time(end) / steps
+        res["peak_bytes_fwd_bwd"] = int(peak)
+        res["input_bytes"] = int(4 * q.numel() * 2)
+        rows.append(res)
+        del q, k, v, g, o, dq, dk, dv, fwd_ws, bwd_ws
+    return {"shape": f"causal bf16 B={B} H={H} C=M=64", "rows": rows,
+            "peak_note": "device memory allocated during one forward + backward call beyond the inputs "
+                         "(O, dQ, dK, dV and both workspaces)"}
 
 
 def time_decode(la, torch, w, steps):
@@ -250,6 +372,15 @@ def main():
             result[key] = {"workload": wn.name, "ms": nms, "tokens_per_s": wn.tokens / (nms / 1000.0),
                            "achieved_GBs": nbytes / (nms * 1e-3) / 1e9,
                            "frac_hbm": nbytes / (nms * 1e-3) / 1e9 / HBM_PEAK_GBS, "kernels": nk}
+    if not args.no_backward:
+        result["backward"] = {}
+        for name in (w.name, "causal_bf16_b16h8n3072"):
+            wb = WORKLOADS[name]
+            log(f"backward {wb.name}")
+            result["backward"][wb.name] = backward_record(la, torch, wb, max(10, args.steps // 2), args.warmup)
+    if not args.no_sweep:
+        log("sequence-length sweep")
+        result["sequence_sweep"] = sequence_sweep(la, torch, 10, 2)
     if not args.no_decode:
         wd = WORKLOADS["decode_f32_s256h8_3072steps"]
         steps = args.decode_steps or wd.steps
