@@ -169,13 +169,42 @@ def time_backward(la, torch, w, steps, warmup):
     return ms, kernels, ms_events
 
 
+def time_train_step(la, torch, w, steps, warmup):
+    """Forward then backward reusing the forward's segment states, per step."""
+    from workloads import backward_inputs
+    q, k, v, g = (t.cuda() for t in backward_inputs(w))
+    o = torch.empty_like(v)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(la.backward_workspace_bytes(w.B, w.H, w.N, q.dtype, w.causal), 1), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        la.forward(q, k, v, causal=w.causal, out=o, workspace=ws)
+        la.backward(q, k, v, g, causal=w.causal, dq=dq, dk=dk, dv=dv, workspace=ws, after_forward=True)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        call()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    del q, k, v, g, o, dq, dk, dv, ws
+    return ms
+
+
 def backward_record(la, torch, w, steps, warmup):
     ms, kernels, ms_events = time_backward(la, torch, w, steps, warmup)
+    train_ms = time_train_step(la, torch, w, steps, warmup)
     eb = 2 if w.dtype == "bf16" else 4
     head_tokens = w.B * w.H * w.N
     row = 64 * eb
     alg = head_tokens * 7 * row  # read Q, K, V, dO; write dQ, dK, dV
     rec = {"workload": w.name, "ms": ms, "ms_with_kernel_events": ms_events,
+           "forward_plus_backward_after_forward_ms": train_ms,
            "tokens_per_s": w.tokens / (ms / 1000.0), "algorithmic_bytes": alg,
            "achieved_GBs": alg / (ms * 1e-3) / 1e9, "frac_hbm": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
            "kernels": kernels}

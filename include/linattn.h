@@ -151,6 +151,26 @@ linattn_status linattn_backward(const void *Q, const void *K, const void *V, con
                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * linattn_backward_after_forward -- linattn_backward for a workspace that
+ * still holds what linattn_forward left in it: the segment states (S, z) at
+ * every segment start, which the backward then does not recompute (saving a
+ * pass over K and V).
+ *
+ * Precondition (not checked): the last call that wrote `workspace` was
+ * linattn_forward with the same Q, K, V contents, B, H, N, dt and causal
+ * flag, on the same device and with the same segment override
+ * (linattn_set_segments).  `workspace` must hold
+ * linattn_backward_workspace_bytes(...) bytes; linattn_forward uses only its
+ * first linattn_forward_workspace_bytes(...).  With a violated precondition
+ * the gradients are wrong; nothing faults.  Other arguments, errors and
+ * results as linattn_backward (the results are bit-identical).
+ */
+linattn_status linattn_backward_after_forward(const void *Q, const void *K, const void *V, const void *dO, void *dQ,
+                                              void *dK, void *dV, int B, int H, int N, int C, int M,
+                                              linattn_dtype dt, int causal, void *workspace, size_t workspace_bytes,
+                                              void *stream);
+
+/*
  * linattn_decode_step -- one constant-state recurrent step for BH independent
  * heads ("Why Replace Attention?", §7.2, steps 1-4; §7.4 constant work per
  * step):

@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.linattn_backward_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
         L.linattn_backward.restype = i
         L.linattn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
+        L.linattn_backward_after_forward.restype = i
+        L.linattn_backward_after_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
         L.linattn_decode_step.restype = i
         L.linattn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
         L.linattn_timer_enable.restype = None
@@ -215,8 +217,14 @@ def backward_workspace_bytes(B: int, H: int, N: int, dtype, causal: bool) -> int
     return int(lib().linattn_backward_workspace_bytes(B, H, N, 64, 64, dt, int(bool(causal))))
 
 
-def backward(q, k, v, grad_out, causal: bool = True, dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """Gradients of ``forward`` (zero initial state) for dL/dO = grad_out; returns (dq, dk, dv)."""
+def backward(q, k, v, grad_out, causal: bool = True, dq=None, dk=None, dv=None, workspace=None, stream=None,
+             after_forward: bool = False):
+    """Gradients of ``forward`` (zero initial state) for dL/dO = grad_out; returns (dq, dk, dv).
+
+    after_forward=True: ``workspace`` (sized by backward_workspace_bytes) was last
+    written by ``forward`` on the same q, k, v and causal flag, and its segment
+    states are reused instead of recomputed.
+    """
     torch = _torch()
     _check_cuda(q, k, v, grad_out, dq, dk, dv)
     B, H, N, C, M = _shape(q, k, v)
@@ -227,9 +235,12 @@ def backward(q, k, v, grad_out, causal: bool = True, dq=None, dk=None, dv=None, 
     dk = torch.empty(k.shape, dtype=k.dtype, device=k.device) if dk is None else dk
     dv = torch.empty(v.shape, dtype=v.dtype, device=v.device) if dv is None else dv
     nbytes = int(lib().linattn_backward_workspace_bytes(B, H, N, C, M, dt, int(bool(causal))))
+    if after_forward and workspace is None:
+        raise LinattnError(8, "after_forward needs the workspace the forward used")
     ws = _alloc_ws(nbytes, q.device, workspace)
-    rc = lib().linattn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(grad_out), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N,
-                                C, M, dt, int(bool(causal)), _ptr(ws), nbytes, _stream(stream))
+    fn = lib().linattn_backward_after_forward if after_forward else lib().linattn_backward
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(grad_out), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, C, M, dt,
+            int(bool(causal)), _ptr(ws), nbytes, _stream(stream))
     _raise(rc)
     return dq, dk, dv
 

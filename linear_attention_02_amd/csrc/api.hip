@@ -153,8 +153,8 @@ linattn_status run_forward(const FwdParams &base, const Plan &plan, int causal, 
 }
 
 template <class E>
-linattn_status run_backward(const BwdParams &base, const BwdPlan &bp, int causal, hipStream_t stream,
-                            linattn_dtype dt) {
+linattn_status run_backward(const BwdParams &base, const BwdPlan &bp, int causal, bool records_ready,
+                            hipStream_t stream, linattn_dtype dt) {
   const Plan &plan = bp.fwd;
   BwdParams p = base;
   p.segments = plan.segments;
@@ -181,7 +181,7 @@ linattn_status run_backward(const BwdParams &base, const BwdPlan &bp, int causal
   const unsigned scan_blocks = (unsigned)((plan.heads * kStateFloats + 255) / 256);
   const unsigned P = (unsigned)plan.segments;
   if (causal) {
-    if (P > 1) {
+    if (P > 1 && !records_ready) {
       {
         TimerScope t(kname("seg_totals", dt), stream);
         hipLaunchKernelGGL(seg_totals_kernel<E>, dim3(heads * (P - 1)), dim3(64), 0, stream, f, (int)P - 1);
@@ -216,16 +216,18 @@ linattn_status run_backward(const BwdParams &base, const BwdPlan &bp, int causal
     }
     if (launch_error("bwd_walk_r") != LINATTN_OK) return LINATTN_ERR_HIP;
   } else {
-    {
-      TimerScope t(kname("seg_totals", dt), stream);
-      hipLaunchKernelGGL(seg_totals_kernel<E>, dim3(heads * P), dim3(64), 0, stream, f, (int)P);
+    if (!records_ready) {
+      {
+        TimerScope t(kname("seg_totals", dt), stream);
+        hipLaunchKernelGGL(seg_totals_kernel<E>, dim3(heads * P), dim3(64), 0, stream, f, (int)P);
+      }
+      if (launch_error("seg_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
+      {
+        TimerScope t("scan", stream);
+        hipLaunchKernelGGL(scan_kernel, dim3(scan_blocks), dim3(256), 0, stream, f, kScanTotal);
+      }
+      if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
     }
-    if (launch_error("seg_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
-    {
-      TimerScope t("scan", stream);
-      hipLaunchKernelGGL(scan_kernel, dim3(scan_blocks), dim3(256), 0, stream, f, kScanTotal);
-    }
-    if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
     {
       TimerScope t(kname("bwd_nc_a", dt), stream);
       hipLaunchKernelGGL(BwdKernels<E>::nc_a, dim3(heads * (unsigned)plan.ranges), dim3(64), 0, stream, p);
@@ -248,7 +250,7 @@ linattn_status run_backward(const BwdParams &base, const BwdPlan &bp, int causal
 
 linattn_status backward_impl(const void *Q, const void *K, const void *V, const void *dO, void *dQ, void *dK,
                              void *dV, int B, int H, int N, int C, int M, linattn_dtype dt, int causal,
-                             void *workspace, size_t workspace_bytes, void *stream) {
+                             bool records_ready, void *workspace, size_t workspace_bytes, void *stream) {
   const long long heads = (long long)B * (long long)H;
   BwdPlan bp;
   if (B >= 0 && H >= 0 && N >= 0)
@@ -273,8 +275,8 @@ linattn_status backward_impl(const void *Q, const void *K, const void *V, const 
   p.stats = reinterpret_cast<f32x2 *>(ws + bp.off_stats);
   p.stats_stride = bp.stats_stride;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (dt == LINATTN_BF16) return run_backward<__bf16>(p, bp, causal, s, dt);
-  return run_backward<float>(p, bp, causal, s, dt);
+  if (dt == LINATTN_BF16) return run_backward<__bf16>(p, bp, causal, records_ready, s, dt);
+  return run_backward<float>(p, bp, causal, records_ready, s, dt);
 }
 
 // Writes S_out/z_out = S0/z0 (or zero) for every head: the N == 0 case of
@@ -390,8 +392,20 @@ linattn_status linattn_backward(const void *Q, const void *K, const void *V, con
                                 void *dV, int B, int H, int N, int C, int M, linattn_dtype dt, int causal,
                                 void *workspace, size_t workspace_bytes, void *stream) {
   try {
-    return backward_impl(Q, K, V, dO, dQ, dK, dV, B, H, N, C, M, dt, causal ? 1 : 0, workspace, workspace_bytes,
-                         stream);
+    return backward_impl(Q, K, V, dO, dQ, dK, dV, B, H, N, C, M, dt, causal ? 1 : 0, false, workspace,
+                         workspace_bytes, stream);
+  } catch (...) {
+    return set_status(LINATTN_ERR_ARG, "internal exception");
+  }
+}
+
+linattn_status linattn_backward_after_forward(const void *Q, const void *K, const void *V, const void *dO, void *dQ,
+                                              void *dK, void *dV, int B, int H, int N, int C, int M,
+                                              linattn_dtype dt, int causal, void *workspace, size_t workspace_bytes,
+                                              void *stream) {
+  try {
+    return backward_impl(Q, K, V, dO, dQ, dK, dV, B, H, N, C, M, dt, causal ? 1 : 0, true, workspace,
+                         workspace_bytes, stream);
   } catch (...) {
     return set_status(LINATTN_ERR_ARG, "internal exception");
   }

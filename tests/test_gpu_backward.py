@@ -138,3 +138,23 @@ def test_named_workload_backward_full_size(name):
     w = WORKLOADS[name]
     q, k, v, g = backward_inputs(w)
     check_backward(q, k, v, g, w.causal, w.dtype, label=name)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("segments", [0, 5])
+def test_backward_after_forward_is_bitwise_identical(dtype, causal, segments):
+    # Reusing the segment states the forward left in the workspace gives the
+    # same bits as recomputing them.
+    B, H, N = 1, 3, 64 * 21 + 9
+    q, k, v = (t.cuda() for t in draw_qkv(B, H, N, 64, 64, dtype, seed=404))
+    g = draw_grad_output(B, H, N, 64, dtype, 404).cuda()
+    la.set_segments(segments)
+    note(f"[grad] after_forward {dtype} causal={causal} segments={la.plan_segments(B, H, N, q.dtype, causal)}")
+    ws = torch.empty(la.backward_workspace_bytes(B, H, N, q.dtype, causal), dtype=torch.uint8, device="cuda")
+    ref = la.backward(q, k, v, g, causal=causal)
+    la.forward(q, k, v, causal=causal, workspace=ws)
+    got = la.backward(q, k, v, g, causal=causal, workspace=ws, after_forward=True)
+    torch.cuda.synchronize()
+    for x, y in zip(got, ref):
+        assert torch.equal(x, y)
