@@ -99,6 +99,18 @@ const char *kname(const char *base, linattn_dtype dt) {
   return s.c_str();
 }
 
+// A totals pass that reads more than the MI355X's 256 MB last-level cache
+// holds uses the streaming load policy (kLoadStreaming); smaller ones keep the
+// data cacheable for the walk that re-reads it.
+constexpr size_t kLastLevelCacheBytes = size_t(256) << 20;
+
+template <class E> using TotalsKernel = void (*)(FwdParams, int);
+template <class E> TotalsKernel<E> totals_kernel(long long heads, long long N) {
+  const size_t pass_bytes = (size_t)heads * (size_t)N * 2 * kD * sizeof(E);
+  if (std::is_same<E, __bf16>::value && pass_bytes > kLastLevelCacheBytes) return seg_totals_kernel<E, kLoadStreaming>;
+  return seg_totals_kernel<E, kLoadDefault>;
+}
+
 template <class E>
 linattn_status run_forward(const FwdParams &base, const Plan &plan, int causal, hipStream_t stream,
                            linattn_dtype dt) {
@@ -112,7 +124,8 @@ linattn_status run_forward(const FwdParams &base, const Plan &plan, int causal, 
     if (plan.segments > 1) {
       {
         TimerScope t(kname("seg_totals", dt), stream);
-        hipLaunchKernelGGL(seg_totals_kernel<E>, dim3(heads * (unsigned)(plan.segments - 1)), dim3(64), 0, stream,
+        hipLaunchKernelGGL(totals_kernel<E>(plan.heads, p.N), dim3(heads * (unsigned)(plan.segments - 1)), dim3(64), 0,
+                           stream,
                            p, plan.segments - 1);
       }
       if (launch_error("seg_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
@@ -133,7 +146,7 @@ linattn_status run_forward(const FwdParams &base, const Plan &plan, int causal, 
   } else {
     {
       TimerScope t(kname("seg_totals", dt), stream);
-      hipLaunchKernelGGL(seg_totals_kernel<E>, dim3(heads * (unsigned)plan.segments), dim3(64), 0, stream, p,
+      hipLaunchKernelGGL(totals_kernel<E>(plan.heads, p.N), dim3(heads * (unsigned)plan.segments), dim3(64), 0, stream, p,
                          plan.segments);
     }
     if (launch_error("seg_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
@@ -184,7 +197,7 @@ linattn_status run_backward(const BwdParams &base, const BwdPlan &bp, int causal
     if (P > 1 && !records_ready) {
       {
         TimerScope t(kname("seg_totals", dt), stream);
-        hipLaunchKernelGGL(seg_totals_kernel<E>, dim3(heads * (P - 1)), dim3(64), 0, stream, f, (int)P - 1);
+        hipLaunchKernelGGL(totals_kernel<E>(plan.heads, p.N), dim3(heads * (P - 1)), dim3(64), 0, stream, f, (int)P - 1);
       }
       if (launch_error("seg_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
       {
@@ -201,7 +214,9 @@ linattn_status run_backward(const BwdParams &base, const BwdPlan &bp, int causal
     if (P > 1) {
       {
         TimerScope t(kname("bwd_reverse_totals", dt), stream);
-        hipLaunchKernelGGL(BwdKernels<E>::reverse_totals, dim3(heads * (P - 1)), dim3(64), 0, stream, p);
+        const bool streaming = (size_t)plan.heads * (size_t)p.N * 2 * kD * sizeof(E) > kLastLevelCacheBytes;
+        hipLaunchKernelGGL(streaming ? BwdKernels<E>::reverse_totals_streaming : BwdKernels<E>::reverse_totals,
+                           dim3(heads * (P - 1)), dim3(64), 0, stream, p);
       }
       if (launch_error("bwd_reverse_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
       {
@@ -219,7 +234,7 @@ linattn_status run_backward(const BwdParams &base, const BwdPlan &bp, int causal
     if (!records_ready) {
       {
         TimerScope t(kname("seg_totals", dt), stream);
-        hipLaunchKernelGGL(seg_totals_kernel<E>, dim3(heads * P), dim3(64), 0, stream, f, (int)P);
+        hipLaunchKernelGGL(totals_kernel<E>(plan.heads, p.N), dim3(heads * P), dim3(64), 0, stream, f, (int)P);
       }
       if (launch_error("seg_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
       {

@@ -380,7 +380,7 @@ __device__ inline void reverse_sums(State &acc, const Frag<E> qr[NT][4], const F
   }
 }
 
-template <class E> __device__ inline void bwd_reverse_totals(const BwdParams &p) {
+template <class E, int kPolicy> __device__ inline void bwd_reverse_totals(const BwdParams &p) {
   const int worker = blockIdx.x;
   const int h = worker % p.heads;
   const int s = 1 + worker / p.heads;
@@ -401,7 +401,7 @@ template <class E> __device__ inline void bwd_reverse_totals(const BwdParams &p)
     __shared__ u32x4 slot[Slot<2, NT>::kVec + 8 * NT];
     u32x4 *sreg = slot + Slot<2, NT>::kVec;
     const __bf16 *src[2] = {Qh, Gh};
-    stage_issue<2, NT>(slot, src, t_begin, chunk_rows(t_begin, t_end), n16, g);
+    stage_issue<2, NT, kPolicy>(slot, src, t_begin, chunk_rows(t_begin, t_end), n16, g);
     stage_stats<NT>(sreg, stats_h, t_begin, chunk_rows(t_begin, t_end), lane);
     for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
       const int rows = chunk_rows(t0, t_end);
@@ -419,7 +419,7 @@ template <class E> __device__ inline void bwd_reverse_totals(const BwdParams &p)
       }
       wait_lgkmcnt0();
       if (t0 + kChunk < t_end) {
-        stage_issue<2, NT>(slot, src, t0 + kChunk, chunk_rows(t0 + kChunk, t_end), n16, g);
+        stage_issue<2, NT, kPolicy>(slot, src, t0 + kChunk, chunk_rows(t0 + kChunk, t_end), n16, g);
         stage_stats<NT>(sreg, stats_h, t0 + kChunk, chunk_rows(t0 + kChunk, t_end), lane);
       }
       if (rows < kChunk) {
@@ -461,8 +461,13 @@ template <class E> __device__ inline void bwd_reverse_totals(const BwdParams &p)
   state_store_record(acc, p.wsR + ((long long)h * p.recR + s) * kStateFloats, lane, n16, g);
 }
 
-__global__ __launch_bounds__(64, 1) void bwd_reverse_totals_kernel_bf16(BwdParams p) { bwd_reverse_totals<__bf16>(p); }
-__global__ __launch_bounds__(64, 1) void bwd_reverse_totals_kernel_f32(BwdParams p) { bwd_reverse_totals<float>(p); }
+template <int kPolicy>
+__global__ __launch_bounds__(64, 1) void bwd_reverse_totals_kernel_bf16(BwdParams p) {
+  bwd_reverse_totals<__bf16, kPolicy>(p);
+}
+__global__ __launch_bounds__(64, 1) void bwd_reverse_totals_kernel_f32(BwdParams p) {
+  bwd_reverse_totals<float, kLoadDefault>(p);
+}
 
 // ---------------------------------------------------------------------------
 // Right-to-left walk: dK and dV from the suffix state (R, r).
@@ -958,7 +963,8 @@ __global__ __launch_bounds__(64, 1) void bwd_nc_b_kernel_f32(BwdParams p) { bwd_
 template <class E> struct BwdKernels;
 template <> struct BwdKernels<__bf16> {
   static constexpr auto walk_f = bwd_walk_f_kernel_bf16;
-  static constexpr auto reverse_totals = bwd_reverse_totals_kernel_bf16;
+  static constexpr auto reverse_totals = bwd_reverse_totals_kernel_bf16<kLoadDefault>;
+  static constexpr auto reverse_totals_streaming = bwd_reverse_totals_kernel_bf16<kLoadStreaming>;
   static constexpr auto walk_r = bwd_walk_r_kernel_bf16;
   static constexpr auto nc_a = bwd_nc_a_kernel_bf16;
   static constexpr auto nc_b = bwd_nc_b_kernel_bf16;
@@ -966,6 +972,7 @@ template <> struct BwdKernels<__bf16> {
 template <> struct BwdKernels<float> {
   static constexpr auto walk_f = bwd_walk_f_kernel_f32;
   static constexpr auto reverse_totals = bwd_reverse_totals_kernel_f32;
+  static constexpr auto reverse_totals_streaming = bwd_reverse_totals_kernel_f32;
   static constexpr auto walk_r = bwd_walk_r_kernel_f32;
   static constexpr auto nc_a = bwd_nc_a_kernel_f32;
   static constexpr auto nc_b = bwd_nc_b_kernel_f32;

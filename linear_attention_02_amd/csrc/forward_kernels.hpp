@@ -196,9 +196,16 @@ template <int N> __device__ inline void wait_vmcnt() {
 }
 __device__ inline void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
 
+// Cache policy of the staging loads.  kLoadStreaming sets the non-temporal
+// bit: measured on MI355X, a pass over data much larger than the 256 MB
+// last-level cache reads faster with it, while data that fits is better left
+// cacheable so that a following pass over the same tensors hits the cache.
+constexpr int kLoadDefault = 0;
+constexpr int kLoadStreaming = 2;
+
 // Fetch rows [t0, t0 + rows) of the given tensors into the slot (chunks of
 // NT row tiles of 16 tokens).
-template <int kTensors, int NT = 4>
+template <int kTensors, int NT = 4, int kPolicy = kLoadDefault>
 __device__ inline void stage_issue(u32x4 *slot, const __bf16 *const src[kTensors], long long t0, int rows, int n16,
                                    int g) {
   const int lane = 16 * g + n16;
@@ -211,7 +218,7 @@ __device__ inline void stage_issue(u32x4 *slot, const __bf16 *const src[kTensors
       const int row = 8 * i + sub;
       if (row < rows)
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4 *>(src[tsr] + (t0 + row) * kD) + piece,
-                                         (lds_void *)(slot + (tsr * 2 * NT + i) * 64), 16, 0, 0);
+                                         (lds_void *)(slot + (tsr * 2 * NT + i) * 64), 16, 0, kPolicy);
     }
   }
 }
@@ -247,11 +254,11 @@ __device__ inline Frag<__bf16> lds_tok_frag(const u32x4 *slot, int tsr, int jt, 
 // Walks the chunks [t_begin, t_end): body(slot, t0, rows) runs on each chunk
 // while the next one streams into the slot.  kStores is the number of
 // vector-memory stores body() issues on a full chunk.
-template <int kTensors, int kStores, class Body>
+template <int kTensors, int kStores, int kPolicy, class Body>
 __device__ inline void stream_lds(u32x4 *slot, const __bf16 *const src[kTensors], long long t_begin, long long t_end,
                                   int n16, int g, Body &&body) {
   if (t_begin >= t_end) return;
-  stage_issue<kTensors>(slot, src, t_begin, chunk_rows(t_begin, t_end), n16, g);
+  stage_issue<kTensors, 4, kPolicy>(slot, src, t_begin, chunk_rows(t_begin, t_end), n16, g);
   for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
     const int rows = chunk_rows(t0, t_end);
     // Outstanding vector-memory operations: this chunk's loads, then the
@@ -400,7 +407,7 @@ __device__ inline void store_rows(E *Oh, long long row0, int rows_left, const f3
 // ---------------------------------------------------------------------------
 // Pass 1: per-segment totals of phi(K)^T V and phi(K).
 // ---------------------------------------------------------------------------
-template <class E>
+template <class E, int kPolicy = kLoadDefault>
 __global__ __launch_bounds__(64, 1) void seg_totals_kernel(FwdParams p, int total_segments) {
   const int worker = blockIdx.x;
   const int h = worker % p.heads;
@@ -420,7 +427,7 @@ __global__ __launch_bounds__(64, 1) void seg_totals_kernel(FwdParams p, int tota
   if constexpr (std::is_same<E, __bf16>::value) {
     __shared__ u32x4 slot[Slot<2>::kVec];
     const __bf16 *src[2] = {Kh, Vh};
-    stream_lds<2, 0>(slot, src, t_begin, t_end, n16, g, [&](const u32x4 *sl, long long t0, int rows) {
+    stream_lds<2, 0, kPolicy>(slot, src, t_begin, t_end, n16, g, [&](const u32x4 *sl, long long t0, int rows) {
       (void)t0;
       Frag<E> kt[4][4], vt[4][4];
 #pragma unroll
@@ -431,7 +438,8 @@ __global__ __launch_bounds__(64, 1) void seg_totals_kernel(FwdParams p, int tota
           vt[jt][c] = lds_tok_frag(sl, 1, jt, c, lane);
         }
       wait_lgkmcnt0();
-      if (t0 + kChunk < t_end) stage_issue<2>(slot, src, t0 + kChunk, chunk_rows(t0 + kChunk, t_end), n16, g);
+      if (t0 + kChunk < t_end)
+        stage_issue<2, 4, kPolicy>(slot, src, t0 + kChunk, chunk_rows(t0 + kChunk, t_end), n16, g);
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
