@@ -13,6 +13,8 @@ inputs resident in HBM.  The same run also times
   * the non-causal forward on B=8, H=8, N=4096,
   * the backward (dQ, dK, dV) of the headline and CIFAR-shaped workloads,
   * forward and forward+backward time and peak memory for N = 2^9..2^16,
+  * images/s of greedy generation with a random-weight 12-layer shell
+    (3072 steps for 256 images, attention through the decode step),
   * the fp64 CPU oracle on a bounded sample of the headline workload
     (`cpu_baseline`, rank 0 only).
 `roofline` is for the dominant kernel (the causal walk): algorithmic bytes
@@ -78,6 +80,7 @@ def parse_args():
     ap.add_argument("--no-noncausal", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-generation", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens per head of the headline workload the oracle runs on (0 = all)")
@@ -277,6 +280,29 @@ def sequence_sweep(la, torch, steps, warmup, B=1, H=8, exps=range(9, 17)):
                          "(O, dQ, dK, dV and both workspaces)"}
 
 
+def time_generation(torch, cfg, dtype):
+    """Greedy generation of cfg.steps tokens for cfg.batch sequences with the
+    random-weight shell, one HIP-graph replay per step; returns images/s and
+    ms per step."""
+    from linear_attention_02_amd.generation import GenerationShell
+    from workloads import draw_shell_weights
+    sh = GenerationShell(draw_shell_weights(cfg), cfg.layers, cfg.d_model, cfg.heads, cfg.batch, dtype=dtype)
+    sh.capture()
+    first = torch.zeros(cfg.batch, dtype=torch.int64)
+    sh.generate(16, first)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    sh.generate(cfg.steps, first)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    ok = bool(torch.isfinite(sh.logits).all())
+    del sh
+    return {"images_per_s": cfg.batch / (ms / 1000.0), "ms_per_step": ms / cfg.steps, "total_s": ms / 1000.0,
+            "finite": ok}
+
+
 def time_decode(la, torch, w, steps):
     from workloads import decode_inputs
     heads = w.heads
@@ -410,6 +436,18 @@ def main():
     if not args.no_sweep:
         log("sequence-length sweep")
         result["sequence_sweep"] = sequence_sweep(la, torch, 10, 2)
+    if not args.no_generation:
+        from workloads import SHELLS
+        cfg = SHELLS["shell_l12_d512_h8_b256_3072steps"]
+        gen = {"workload": cfg.name, "layers": cfg.layers, "d_model": cfg.d_model, "heads": cfg.heads,
+               "batch": cfg.batch, "steps": cfg.steps,
+               "note": "random weights; greedy decoding; one HIP-graph replay per step; attention through "
+                       "linattn_decode_step, dense parts through library GEMMs; the pages' 17.85 images/s "
+                       "(2020 hardware, trained CIFAR-10 model) is context, not a comparable target"}
+        for key, dt in (("bf16", torch.bfloat16), ("f32", torch.float32)):
+            log(f"generation {cfg.name} {key}")
+            gen[key] = time_generation(torch, cfg, dt)
+        result["generation"] = gen
     if not args.no_decode:
         wd = WORKLOADS["decode_f32_s256h8_3072steps"]
         steps = args.decode_steps or wd.steps
@@ -425,6 +463,19 @@ def main():
                             "bytes_per_step": state_bytes + io_bytes,
                             "note": "one kernel per step, 3072 launches replayed from one HIP graph; the 34 MB "
                                     "state can stay in the MI355X's 256 MB last-level cache between steps"}
+        # The same step with 8x the sequences: 272 MB of state, more than the
+        # last-level cache holds, so every step moves it through HBM.
+        from workloads import DecodeWorkload
+        wc = DecodeWorkload("decode_f32_s2048h8_cold", "f32", 8 * wd.sequences, wd.H, 64, seed=wd.seed)
+        log(f"decode {wc.name}: {wc.steps} steps")
+        total_c = time_decode(la, torch, wc, wc.steps)
+        per_c = total_c / wc.steps
+        sb = wc.heads * (wc.C * wc.M + wc.C) * 4 * 2
+        result["decode"]["cold"] = {"workload": wc.name, "heads": wc.heads, "steps": wc.steps,
+                                    "us_per_step": per_c * 1000.0,
+                                    "tokens_per_s": wc.sequences * wc.steps / (total_c / 1000.0),
+                                    "state_GBs": sb / (per_c * 1e-3) / 1e9,
+                                    "frac_hbm_state": sb / (per_c * 1e-3) / 1e9 / HBM_PEAK_GBS}
     if args.copy_calibration:
         n = 1 << 28
         a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)

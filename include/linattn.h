@@ -188,6 +188,23 @@ linattn_status linattn_decode_step(float *S, float *z, const void *q, const void
                                    int BH, int C, int M, linattn_dtype dt, void *stream);
 
 /*
+ * linattn_decode_step_strided -- linattn_decode_step with the q, k and v
+ * vectors of consecutive heads `row_stride` elements apart instead of 64, so
+ * that they can be column slices of one projection output: with a q/k/v
+ * projection whose columns are ordered (head, {q, k, v}, 64), q = out,
+ * k = out + 64, v = out + 128 and row_stride = 192.
+ *
+ * row_stride: >= 64, and row_stride * element size a multiple of 16 bytes.
+ * q, k, v: head h's vector at q + h * row_stride (likewise k, v), in `dt`;
+ *   they may overlap each other, but not S, z or o.
+ * Other arguments, layouts and errors as linattn_decode_step (SHAPE for a
+ * bad stride, ALIGN for a misaligned one).
+ */
+linattn_status linattn_decode_step_strided(float *S, float *z, const void *q, const void *k, const void *v, float *o,
+                                           int BH, int C, int M, linattn_dtype dt, long long row_stride,
+                                           void *stream);
+
+/*
  * Kernel timer (measurement support).  When enabled, the library brackets
  * each kernel it launches with HIP events recorded on the launch stream and,
  * when linattn_timer_read() is called, adds up the elapsed times per kernel

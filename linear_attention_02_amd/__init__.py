@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.linattn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
         L.linattn_backward_after_forward.restype = i
         L.linattn_backward_after_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
+        L.linattn_decode_step_strided.restype = i
+        L.linattn_decode_step_strided.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, ctypes.c_longlong, vp]
         L.linattn_decode_step.restype = i
         L.linattn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
         L.linattn_timer_enable.restype = None
@@ -305,3 +307,32 @@ def set_segments(n: int) -> int:
 def plan_segments(B: int, H: int, N: int, dtype, causal: bool) -> int:
     dt = F32 if str(dtype).endswith("float32") else BF16
     return int(lib().linattn_plan_segments(B, H, N, dt, int(bool(causal))))
+
+
+def decode_step_strided(S, z, q, k, v, out=None, stream=None):
+    """decode_step for q, k, v given as [BH, 64] views that share one row
+    stride (e.g. column slices of a [BH, 3 * 64] projection output)."""
+    torch = _torch()
+    _check_cuda(S, z, out)
+    for t in (q, k, v):
+        if not t.is_cuda:
+            raise LinattnError(8, "tensors must be on a GPU device (no CPU fallback exists)")
+        if t.dim() != 2 or t.stride(1) != 1:
+            raise LinattnError(2, "q, k, v must be 2-D with unit column stride")
+    stride = q.stride(0)
+    if k.stride(0) != stride or v.stride(0) != stride:
+        raise LinattnError(2, "q, k and v must share one row stride")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise LinattnError(3, "q, k and v must share one dtype")
+    if S.dtype != torch.float32 or z.dtype != torch.float32:
+        raise LinattnError(3, "S and z are float32")
+    BH, C = q.shape
+    M = v.shape[1]
+    if k.shape != q.shape or v.shape[0] != BH or S.numel() != BH * C * M or z.numel() != BH * C:
+        raise LinattnError(2, "decode_step_strided shape mismatch")
+    if out is None:
+        out = torch.empty((BH, M), dtype=torch.float32, device=q.device)
+    rc = lib().linattn_decode_step_strided(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), BH, C, M,
+                                           _dt(q), int(stride), _stream(stream))
+    _raise(rc)
+    return out

@@ -426,28 +426,49 @@ linattn_status linattn_backward_after_forward(const void *Q, const void *K, cons
   }
 }
 
+}  // extern "C"
+
+namespace {
+linattn_status decode_impl(float *S, float *z, const void *q, const void *k, const void *v, float *o, int BH, int C,
+                           int M, linattn_dtype dt, long long stride, void *stream) {
+  const Check c = check_decode(S, z, q, k, v, o, BH, C, M, dt, stride);
+  if (!c.ok()) return from_check(c);
+  if (BH == 0) return set_status(LINATTN_OK, "");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const unsigned blocks = (unsigned)((BH + 3) / 4);
+  {
+    TimerScope t(kname("decode_step", dt), s);
+    if (dt == LINATTN_BF16) {
+      hipLaunchKernelGGL(decode_step_kernel<__bf16>, dim3(blocks), dim3(256), 0, s, S, z,
+                         reinterpret_cast<const __bf16 *>(q), reinterpret_cast<const __bf16 *>(k),
+                         reinterpret_cast<const __bf16 *>(v), o, BH, stride);
+    } else {
+      hipLaunchKernelGGL(decode_step_kernel<float>, dim3(blocks), dim3(256), 0, s, S, z,
+                         reinterpret_cast<const float *>(q), reinterpret_cast<const float *>(k),
+                         reinterpret_cast<const float *>(v), o, BH, stride);
+    }
+  }
+  if (launch_error("decode_step") != LINATTN_OK) return LINATTN_ERR_HIP;
+  return set_status(LINATTN_OK, "");
+}
+}  // namespace
+
+extern "C" {
+
 linattn_status linattn_decode_step(float *S, float *z, const void *q, const void *k, const void *v, float *o, int BH,
                                    int C, int M, linattn_dtype dt, void *stream) {
   try {
-    const Check c = check_decode(S, z, q, k, v, o, BH, C, M, dt);
-    if (!c.ok()) return from_check(c);
-    if (BH == 0) return set_status(LINATTN_OK, "");
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const unsigned blocks = (unsigned)((BH + 3) / 4);
-    {
-      TimerScope t(kname("decode_step", dt), s);
-      if (dt == LINATTN_BF16) {
-        hipLaunchKernelGGL(decode_step_kernel<__bf16>, dim3(blocks), dim3(256), 0, s, S, z,
-                           reinterpret_cast<const __bf16 *>(q), reinterpret_cast<const __bf16 *>(k),
-                           reinterpret_cast<const __bf16 *>(v), o, BH);
-      } else {
-        hipLaunchKernelGGL(decode_step_kernel<float>, dim3(blocks), dim3(256), 0, s, S, z,
-                           reinterpret_cast<const float *>(q), reinterpret_cast<const float *>(k),
-                           reinterpret_cast<const float *>(v), o, BH);
-      }
-    }
-    if (launch_error("decode_step") != LINATTN_OK) return LINATTN_ERR_HIP;
-    return set_status(LINATTN_OK, "");
+    return decode_impl(S, z, q, k, v, o, BH, C, M, dt, 64, stream);
+  } catch (...) {
+    return set_status(LINATTN_ERR_ARG, "internal exception");
+  }
+}
+
+linattn_status linattn_decode_step_strided(float *S, float *z, const void *q, const void *k, const void *v, float *o,
+                                           int BH, int C, int M, linattn_dtype dt, long long row_stride,
+                                           void *stream) {
+  try {
+    return decode_impl(S, z, q, k, v, o, BH, C, M, dt, row_stride, stream);
   } catch (...) {
     return set_status(LINATTN_ERR_ARG, "internal exception");
   }

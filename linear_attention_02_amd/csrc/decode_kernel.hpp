@@ -10,7 +10,9 @@
 // (m4, cq) = (l & 15, l >> 4) holds columns 4*m4..4*m4+3 of rows 16*cq..16*cq+15,
 // so each 16-byte load or store instruction covers four whole 256-byte rows.
 // The column sums phi(q)^T S are reduced across the four row groups with
-// cross-lane shuffles; phi(q)^T z with a full-wave reduction.
+// cross-lane shuffles; phi(q)^T z with a full-wave reduction.  The q, k and v
+// vectors of consecutive heads are `stride` elements apart (64 when they are
+// packed; larger when they are column slices of one projection output).
 #pragma once
 
 #include "device_common.hpp"
@@ -27,15 +29,15 @@ template <class E>
 __global__ __launch_bounds__(256) void decode_step_kernel(float *__restrict__ S, float *__restrict__ z,
                                                           const E *__restrict__ q, const E *__restrict__ k,
                                                           const E *__restrict__ v, float *__restrict__ o,
-                                                          int heads) {
+                                                          int heads, long long stride) {
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (h >= heads) return;
   const int lane = threadIdx.x & 63;
   const int m4 = lane & 15, cq = lane >> 4;
 
-  const E *qh = q + (long long)h * kD;
-  const E *kh = k + (long long)h * kD;
-  const E *vh = v + (long long)h * kD;
+  const E *qh = q + (long long)h * stride;
+  const E *kh = k + (long long)h * stride;
+  const E *vh = v + (long long)h * stride;
   float4 *Sh = reinterpret_cast<float4 *>(S + (long long)h * kD * kD);
 
   // phi(k), phi(q) for this lane's 16 rows; v for its 4 columns.

@@ -209,18 +209,22 @@ Check check_state_args(const float *S0, const float *z0, const float *S_out, con
 }
 
 Check check_decode(const float *S, const float *z, const void *q, const void *k, const void *v, const float *o,
-                   int BH, int C, int M, linattn_dtype dt) {
+                   int BH, int C, int M, linattn_dtype dt, long long stride) {
   const size_t eb = dtype_bytes(dt);
   if (eb == 0) return fail(LINATTN_ERR_DTYPE, "unknown element type");
   if (BH < 0) return fail(LINATTN_ERR_SHAPE, "BH must be non-negative");
   if (C != 64 || M != 64) return fail(LINATTN_ERR_SHAPE, "only C = M = 64 is supported");
+  if (stride < 64) return fail(LINATTN_ERR_SHAPE, "the row stride of q, k and v must be at least 64");
+  if (stride > (long long)(SIZE_MAX / 16) / (BH > 0 ? BH : 1)) return fail(LINATTN_ERR_SHAPE, "stride overflows");
   if (BH == 0) return Check();
   if (!S || !z || !q || !k || !v || !o) return fail(LINATTN_ERR_NULL, "S, z, q, k, v and o must be non-NULL");
+  if ((stride * (long long)eb) % 16 != 0) return fail(LINATTN_ERR_ALIGN, "the row stride must be a multiple of 16 bytes");
   for (const void *p : {(const void *)S, (const void *)z, q, k, v, (const void *)o})
     if (!aligned16(p)) return fail(LINATTN_ERR_ALIGN, "decode buffers must be 16-byte aligned");
   const size_t n = (size_t)BH;
   const Buffer bS{S, n * 4096 * 4, "S"}, bz{z, n * 64 * 4, "z"}, bo{o, n * 64 * 4, "o"};
-  const Buffer bq{q, n * 64 * eb, "q"}, bk{k, n * 64 * eb, "k"}, bv{v, n * 64 * eb, "v"};
+  const size_t span = ((n - 1) * (size_t)stride + 64) * eb;  // first to last element of the rows
+  const Buffer bq{q, span, "q"}, bk{k, span, "k"}, bv{v, span, "v"};
   if (overlaps(bS, bz) || overlaps(bo, bS) || overlaps(bo, bz))
     return fail(LINATTN_ERR_ALIAS, "S, z and o must not overlap");
   for (const Buffer *in : {&bq, &bk, &bv})

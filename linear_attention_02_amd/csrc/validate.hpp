@@ -69,8 +69,9 @@ Check check_state_args(const float *S0, const float *z0, const float *S_out, con
                        const void *Q, const void *K, const void *V, const void *O, size_t qk_bytes,
                        size_t vo_bytes, const void *workspace, size_t workspace_bytes);
 
+// q, k, v rows of consecutive heads are `stride` elements apart (>= 64).
 Check check_decode(const float *S, const float *z, const void *q, const void *k, const void *v, const float *o,
-                   int BH, int C, int M, linattn_dtype dt);
+                   int BH, int C, int M, linattn_dtype dt, long long stride = 64);
 
 bool overlaps(const Buffer &a, const Buffer &b);
 

@@ -101,6 +101,17 @@ def test_decode_rejects_bad_arguments(L):
     assert d(S, z, S, k, v, o, 4, 64, 64, 0, None) == ALIAS          # q inside S
 
 
+def test_strided_decode_rejects_bad_arguments(L):
+    d = L.linattn_decode_step_strided
+    S, z, q, o = 0x100000, 0x200000, 0x300000, 0x600000
+    assert d(S, z, q, q + 128, q + 256, o, 4, 64, 64, 1, 32, None) == SHAPE      # stride < 64
+    assert d(S, z, q, q + 128, q + 256, o, 4, 64, 64, 1, 100, None) == ALIGN     # 200 bytes, not 16-aligned
+    assert d(S, z, None, q + 128, q + 256, o, 4, 64, 64, 1, 192, None) == NULL
+    # rows of head 3 reach 3 * 192 * 2 + 128 bytes past q: S placed there overlaps
+    assert d(q + 1088, z, q, q + 128, q + 256, o, 4, 64, 64, 1, 192, None) == ALIAS
+    assert d(S, z, q, q + 128, q + 256, o, 0, 64, 64, 1, 192, None) == OK
+
+
 def test_planner_segments(L):
     # Few heads, long sequences: split so the grid covers the device.
     assert L.linattn_plan_segments(2, 8, 131072, 1, 1) > 1

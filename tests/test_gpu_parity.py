@@ -241,3 +241,21 @@ def test_named_decode_workload_full_size_sampled_heads():
     note(f"[parity] {w.name} worst={worst:.3e}")
     assert worst <= TOL["f32"]
     assert np.max(np.abs(S[sample].cpu().double().numpy() - S_ref) / S_mag) < 1e-4
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_strided_decode_matches_packed_decode(dtype):
+    # q, k, v as column slices of one [BH, 192] buffer give the same bits as
+    # packed [BH, 64] operands.
+    heads = 37
+    g = torch.Generator().manual_seed(77)
+    rows = torch.randn(heads, 192, generator=g).to(torch.bfloat16 if dtype == "bf16" else torch.float32).cuda()
+    S0 = torch.randn(heads, 64, 64, generator=g).abs().cuda()
+    z0 = torch.rand(heads, 64, generator=g).cuda() + 1.0
+    S1, z1, S2, z2 = S0.clone(), z0.clone(), S0.clone(), z0.clone()
+    note(f"[parity] strided decode {dtype} heads={heads}")
+    a = la.decode_step(S1, z1, rows[:, 0:64].contiguous(), rows[:, 64:128].contiguous(),
+                       rows[:, 128:192].contiguous())
+    b = la.decode_step_strided(S2, z2, rows[:, 0:64], rows[:, 64:128], rows[:, 128:192])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(S1, S2) and torch.equal(z1, z2)

@@ -146,3 +146,61 @@ def backward_inputs(w: ForwardWorkload):
     """Q, K, V of the forward workload plus a dL/dO of V's shape."""
     q, k, v = forward_inputs(w)
     return q, k, v, draw_grad_output(w.B, w.H, w.N, w.M, w.dtype, w.seed)
+
+
+# ---------------------------------------------------------------------------
+# Generation shell: a random-weight stack of linear-attention layers that
+# emits one pixel-channel per step, shaped like autoregressive CIFAR-10
+# generation (3072 steps per image, 256 values per step; "Transformers Are
+# RNNs: Linear Attention" knowledge note, "How we know") with the running
+# model's d_model 512, h 8, 12 layers ("Why Replace Attention?", "The Running
+# Example").  The weights are random: throughput does not depend on them, and
+# no trained model is available.
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class ShellConfig:
+    name: str
+    layers: int = 12
+    d_model: int = 512
+    heads: int = 8
+    d_ff: int = 2048
+    vocab: int = 256
+    steps: int = 3072
+    batch: int = 256
+    seed: int = 2001
+
+
+SHELLS: Dict[str, ShellConfig] = {
+    "shell_l12_d512_h8_b256_3072steps": ShellConfig("shell_l12_d512_h8_b256_3072steps"),
+}
+
+
+def draw_shell_weights(cfg: ShellConfig) -> Dict[str, torch.Tensor]:
+    """float32 CPU weights: token and position embeddings, per layer the fused
+    q/k/v projection, the output projection and the two feed-forward matrices
+    (all N(0, 0.02^2), scaled by 1/sqrt(2 * layers) on the residual outputs),
+    layer-norm gains 1 and biases 0, and the output head."""
+    g = torch.Generator("cpu").manual_seed(int(cfg.seed))
+    D, F, L = cfg.d_model, cfg.d_ff, cfg.layers
+
+    def n(*shape, std=0.02):
+        return (torch.randn(shape, dtype=torch.float32, generator=g) * std).contiguous()
+
+    res = 0.02 / (2.0 * max(L, 1)) ** 0.5
+    w = {"tok_emb": n(cfg.vocab, D), "pos_emb": n(cfg.steps, D), "head": n(D, cfg.vocab),
+         "ln_f_g": torch.ones(D), "ln_f_b": torch.zeros(D)}
+    for l in range(L):
+        w[f"wqkv{l}"] = n(D, 3 * D)
+        w[f"wo{l}"] = n(D, D, std=res)
+        w[f"w1{l}"] = n(D, F)
+        w[f"w2{l}"] = n(F, D, std=res)
+        for k in ("ln1", "ln2"):
+            w[f"{k}_g{l}"] = torch.ones(D)
+            w[f"{k}_b{l}"] = torch.zeros(D)
+    return w
+
+
+def shell_teacher_tokens(cfg: ShellConfig, batch: int, steps: int, seed: int) -> torch.Tensor:
+    """Fixed input tokens [steps, batch] for teacher-forced comparisons."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    return torch.randint(0, cfg.vocab, (steps, batch), generator=g, dtype=torch.int64)
