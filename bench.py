@@ -354,8 +354,16 @@ def cpu_baseline(w, sample_tokens, host_inputs):
     t0 = time.perf_counter()
     oracle.forward_recurrent(q, k, v, causal=w.causal, threads=threads)
     dt = time.perf_counter() - t0
+    # The same oracle on one core, over the first n1 tokens of every head.
+    n1 = min(n, 8192)
+    q1, k1, v1 = (to_oracle_array(t[:, :, :n1].contiguous()) for t in host_inputs)
+    t1 = time.perf_counter()
+    oracle.forward_recurrent(q1, k1, v1, causal=w.causal, threads=1)
+    d1 = time.perf_counter() - t1
+    single = {"value": w.B * n1 / d1, "unit": "tokens/s", "cores": 1, "seconds": d1,
+              "sample": f"first {n1} tokens of every head of {w.name}"}
     return {"value": w.B * n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "seconds": dt,
+            "seconds": dt, "single_core": single,
             "sample": f"fp64 C oracle (causal recurrence, O(N) per head) on the first {n} of {w.N} tokens of every "
                       f"head of {w.name} (B={w.B}, H={w.H}, same host inputs as the GPU run); tokens/s counts "
                       f"B*{n} positions over the wall time, threads over (batch, head)"}
