@@ -72,6 +72,45 @@ int main() {
   EXPECT(check_decode(S, z, P(0x400000), P(0x500000), P(0x600000), z, 8, 64, 64, LINATTN_F32).status ==
          LINATTN_ERR_ALIAS);
 
+  // Strided decode: row stride, its alignment, and the span of strided rows.
+  EXPECT(check_decode(S, z, P(0x400000), P(0x400080), P(0x400100), o, 8, 64, 64, LINATTN_BF16, 192).ok());
+  EXPECT(check_decode(S, z, P(0x400000), P(0x400080), P(0x400100), o, 8, 64, 64, LINATTN_BF16, 32).status ==
+         LINATTN_ERR_SHAPE);
+  EXPECT(check_decode(S, z, P(0x400000), P(0x400080), P(0x400100), o, 8, 64, 64, LINATTN_BF16, 100).status ==
+         LINATTN_ERR_ALIGN);
+  // 8 heads x 192 bf16 = 3 KB of rows from q: o placed 2 KB after q overlaps them.
+  EXPECT(check_decode(S, z, P(0x400000), P(0x400080), P(0x400100), (const float *)P(0x400800), 8, 64, 64,
+                      LINATTN_BF16, 192).status == LINATTN_ERR_ALIAS);
+  EXPECT(check_decode(S, z, P(0x400000), P(0x400080), P(0x400100), o, 8, 64, 64, LINATTN_BF16, 1LL << 62).status ==
+         LINATTN_ERR_SHAPE);
+
+  // Backward plan: two record sets and the per-token pairs, each 256-byte aligned.
+  {
+    BwdPlan b = plan_backward(16, 131072, 1, 256, 0);
+    EXPECT(b.fwd.segments == 64 && b.recR == 64 && b.stats_stride == 131072);
+    EXPECT(b.off_r % 256 == 0 && b.off_stats % 256 == 0 && b.off_r >= b.fwd.workspace_bytes);
+    EXPECT(b.workspace_bytes == b.off_stats + (size_t)16 * 131072 * 8);
+    b = plan_backward(4, 100, 1, 256, 0);  // ragged N: pairs padded to whole chunks
+    EXPECT(b.stats_stride == 128);
+    b = plan_backward(64, 4096, 0, 256, 0);  // non-causal: ranges + 1 reverse records
+    EXPECT(b.recR == b.fwd.ranges + 1);
+    b = plan_backward(1, 64, 1, 256, 0);  // one segment: no records, pairs only
+    EXPECT(b.fwd.records == 0 && b.recR == 0 && b.workspace_bytes == b.off_stats + 64 * 8);
+  }
+  // Backward argument checks.
+  EXPECT(check_backward(P(0x10000), P(0x20000), P(0x30000), P(0x40000), P(0x50000), P(0x60000), P(0x70000), 1, 1, 64,
+                        64, 64, LINATTN_BF16, nullptr, 0, 0).ok());
+  EXPECT(check_backward(P(0x10000), P(0x20000), P(0x30000), P(0x40000), P(0x50000), P(0x60000), P(0x50010), 1, 1, 64,
+                        64, 64, LINATTN_BF16, nullptr, 0, 0).status == LINATTN_ERR_ALIAS);
+  EXPECT(check_backward(P(0x10000), P(0x20000), P(0x30000), P(0x40000), P(0x40000), P(0x60000), P(0x70000), 1, 1, 64,
+                        64, 64, LINATTN_BF16, nullptr, 0, 0).status == LINATTN_ERR_ALIAS);
+  EXPECT(check_backward(P(0x10000), P(0x20000), P(0x30000), P(0x40000), P(0x50000), P(0x60000), P(0x70000), 1, 1, 64,
+                        64, 64, LINATTN_BF16, P(0x80000), 99, 100).status == LINATTN_ERR_WORKSPACE);
+  EXPECT(check_backward(P(0x10000), P(0x20000), P(0x30000), P(0x40000), P(0x50000), P(0x60000), P(0x70000), 1, 1, 64,
+                        64, 64, LINATTN_BF16, P(0x61000), 4096, 4096).status == LINATTN_ERR_ALIAS);
+  EXPECT(check_backward(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 8, 64, 64, 64,
+                        LINATTN_BF16, nullptr, 0, 0).ok());
+
   // Overlap helper.
   EXPECT(overlaps({P(100), 10, "a"}, {P(109), 1, "b"}));
   EXPECT(!overlaps({P(100), 10, "a"}, {P(110), 1, "b"}));
