@@ -158,3 +158,35 @@ def test_backward_after_forward_is_bitwise_identical(dtype, causal, segments):
     torch.cuda.synchronize()
     for x, y in zip(got, ref):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_tensors_beyond_2_to_the_31_elements_sampled_heads(causal):
+    # 32 x 1024 heads x 1100 tokens x 64: 2.3e9 elements per tensor, so element
+    # offsets pass 2^31.  Forward and backward run on all heads; the oracle
+    # checks sampled heads, among them the last ones (highest addresses).
+    from workloads import draw_device
+    B, H, N = 32, 1024, 1100
+    note(f"[big] B{B} H{H} N{N} causal={causal}: drawing on the device")
+    q = draw_device((B, H, N, 64), "bf16", seed=3101, scale=0.125)
+    k = draw_device((B, H, N, 64), "bf16", seed=3102, scale=0.125)
+    v = draw_device((B, H, N, 64), "bf16", seed=3103)
+    g = draw_device((B, H, N, 64), "bf16", seed=3104)
+    out = la.forward(q, k, v, causal=causal)
+    grads = la.backward(q, k, v, g, causal=causal)
+    torch.cuda.synchronize()
+    note("[big] device work done; checking sampled heads")
+    for head in (0, 12345, B * H - 2, B * H - 1):
+        b, h = divmod(head, H)
+        sl = lambda t: t[b:b + 1, h:h + 1].cpu()
+        arrs = [to_oracle_array(sl(t)) for t in (q, k, v, g)]
+        ref = oracle.forward_recurrent(*arrs[:3], causal=causal)
+        mag = oracle.forward_recurrent(*arrs[:3], causal=causal, absv=True)
+        err, _ = oracle.parity_error(sl(out).double().numpy(), ref, mag)
+        gref = oracle.backward_recurrent(*arrs, causal=causal)
+        gmag = oracle.backward_recurrent(*arrs, causal=causal, companion=True)
+        gerr = [oracle.parity_error(sl(x).double().numpy(), r, m)[0] for x, r, m in zip(grads, gref, gmag)]
+        note(f"[big] head {head}: forward err={err:.3e} grads err={[f'{e:.2e}' for e in gerr]}")
+        assert err <= TOL["bf16"] and max(gerr) <= TOL["bf16"]
+    del q, k, v, g, out, grads
+    torch.cuda.empty_cache()

@@ -204,3 +204,14 @@ def shell_teacher_tokens(cfg: ShellConfig, batch: int, steps: int, seed: int) ->
     """Fixed input tokens [steps, batch] for teacher-forced comparisons."""
     g = torch.Generator("cpu").manual_seed(int(seed))
     return torch.randint(0, cfg.vocab, (steps, batch), generator=g, dtype=torch.int64)
+
+
+def draw_device(shape, dtype: str, seed: int, scale: float = 1.0, device="cuda") -> torch.Tensor:
+    """N(0, 1) (times a power-of-two scale) drawn on the device with its own
+    seeded generator, rounded to the element type: for tensors too large to
+    draw on the host (the random stream differs from the CPU draws)."""
+    g = torch.Generator(device=device).manual_seed(int(seed))
+    x = torch.randn(shape, dtype=torch.float32, device=device, generator=g)
+    if scale != 1.0:
+        x.mul_(scale)
+    return x.to(DTYPES[dtype]).contiguous()
