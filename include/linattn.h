@@ -152,9 +152,10 @@ linattn_status linattn_backward(const void *Q, const void *K, const void *V, con
 
 /*
  * linattn_backward_after_forward -- linattn_backward for a workspace that
- * still holds what linattn_forward left in it: the segment states (S, z) at
- * every segment start, which the backward then does not recompute (saving a
- * pass over K and V).
+ * still holds what linattn_forward left in it: the per-segment (S, z)
+ * records (segment totals, or with more than eight segments per head the
+ * states at every segment start), which the backward then does not recompute
+ * (saving a pass over K and V).
  *
  * Precondition (not checked): the last call that wrote `workspace` was
  * linattn_forward with the same Q, K, V contents, B, H, N, dt and causal

@@ -111,6 +111,25 @@ template <class E> TotalsKernel<E> totals_kernel(long long heads, long long N) {
   return seg_totals_kernel<E, kLoadDefault>;
 }
 
+// One thread per (head, W state elements): W = 4 while that still launches
+// 256 blocks or more, else 1; a batch of eight loads for up to eight records.
+void launch_scan(const FwdParams &p, int mode, hipStream_t stream) {
+  const long long blocks4 = ((long long)p.heads * (kStateFloats / 4) + 255) / 256;
+  const long long blocks1 = ((long long)p.heads * kStateFloats + 255) / 256;
+  const bool small = p.segments <= kScanBatchSmall;
+  if (blocks4 >= 256) {
+    const auto fn = small ? scan_kernel<4, kScanBatchSmall> : scan_kernel<4, kScanBatchLarge>;
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks4), dim3(256), 0, stream, p, mode);
+  } else {
+    const auto fn = small ? scan_kernel<1, kScanBatchSmall> : scan_kernel<1, kScanBatchLarge>;
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks1), dim3(256), 0, stream, p, mode);
+  }
+}
+
+// Causal passes with at most this many segments per head skip the prefix
+// (suffix) scan: each walk wave sums the totals records it needs.
+bool sum_in_walk(int segments) { return segments <= kSumInWalkMaxSegments; }
+
 template <class E>
 linattn_status run_forward(const FwdParams &base, const Plan &plan, int causal, hipStream_t stream,
                            linattn_dtype dt) {
@@ -119,7 +138,6 @@ linattn_status run_forward(const FwdParams &base, const Plan &plan, int causal, 
   p.seg_chunks = plan.seg_chunks;
   p.records = plan.records;
   const unsigned heads = (unsigned)plan.heads;
-  const unsigned scan_blocks = (unsigned)((plan.heads * kStateFloats + 255) / 256);
   if (causal) {
     if (plan.segments > 1) {
       {
@@ -129,12 +147,16 @@ linattn_status run_forward(const FwdParams &base, const Plan &plan, int causal, 
                            p, plan.segments - 1);
       }
       if (launch_error("seg_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
-      {
-        TimerScope t("scan", stream);
-        hipLaunchKernelGGL(scan_kernel, dim3(scan_blocks), dim3(256), 0, stream, p, kScanPrefix);
+      if (sum_in_walk(plan.segments)) {
+        p.init = kInitTotals;
+      } else {
+        {
+          TimerScope t("scan", stream);
+          launch_scan(p, kScanPrefix, stream);
+        }
+        if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
+        p.init = kInitRecord;
       }
-      if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
-      p.init = kInitRecord;
     } else {
       p.init = p.S0 != nullptr ? kInitNatural : kInitZero;
     }
@@ -152,7 +174,7 @@ linattn_status run_forward(const FwdParams &base, const Plan &plan, int causal, 
     if (launch_error("seg_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
     {
       TimerScope t("scan", stream);
-      hipLaunchKernelGGL(scan_kernel, dim3(scan_blocks), dim3(256), 0, stream, p, kScanTotal);
+      launch_scan(p, kScanTotal, stream);
     }
     if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
     {
@@ -191,8 +213,9 @@ linattn_status run_backward(const BwdParams &base, const BwdPlan &bp, int causal
   r.ws = p.wsR;
   r.records = bp.recR;
   const unsigned heads = (unsigned)plan.heads;
-  const unsigned scan_blocks = (unsigned)((plan.heads * kStateFloats + 255) / 256);
   const unsigned P = (unsigned)plan.segments;
+  // The same choice as the forward's, whose records linattn_backward_after_forward reuses.
+  p.sum_in_walk = causal && sum_in_walk(plan.segments) ? 1 : 0;
   if (causal) {
     if (P > 1 && !records_ready) {
       {
@@ -200,11 +223,13 @@ linattn_status run_backward(const BwdParams &base, const BwdPlan &bp, int causal
         hipLaunchKernelGGL(totals_kernel<E>(plan.heads, p.N), dim3(heads * (P - 1)), dim3(64), 0, stream, f, (int)P - 1);
       }
       if (launch_error("seg_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
-      {
-        TimerScope t("scan", stream);
-        hipLaunchKernelGGL(scan_kernel, dim3(scan_blocks), dim3(256), 0, stream, f, kScanPrefix);
+      if (!p.sum_in_walk) {
+        {
+          TimerScope t("scan", stream);
+          launch_scan(f, kScanPrefix, stream);
+        }
+        if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
       }
-      if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
     }
     {
       TimerScope t(kname("bwd_walk_f", dt), stream);
@@ -219,11 +244,13 @@ linattn_status run_backward(const BwdParams &base, const BwdPlan &bp, int causal
                            dim3(heads * (P - 1)), dim3(64), 0, stream, p);
       }
       if (launch_error("bwd_reverse_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
-      {
-        TimerScope t("scan", stream);
-        hipLaunchKernelGGL(scan_kernel, dim3(scan_blocks), dim3(256), 0, stream, r, kScanSuffix);
+      if (!p.sum_in_walk) {
+        {
+          TimerScope t("scan", stream);
+          launch_scan(r, kScanSuffix, stream);
+        }
+        if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
       }
-      if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
     }
     {
       TimerScope t(kname("bwd_walk_r", dt), stream);
@@ -239,7 +266,7 @@ linattn_status run_backward(const BwdParams &base, const BwdPlan &bp, int causal
       if (launch_error("seg_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
       {
         TimerScope t("scan", stream);
-        hipLaunchKernelGGL(scan_kernel, dim3(scan_blocks), dim3(256), 0, stream, f, kScanTotal);
+        launch_scan(f, kScanTotal, stream);
       }
       if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
     }
@@ -251,7 +278,7 @@ linattn_status run_backward(const BwdParams &base, const BwdPlan &bp, int causal
     r.segments = plan.ranges;
     {
       TimerScope t("scan", stream);
-      hipLaunchKernelGGL(scan_kernel, dim3(scan_blocks), dim3(256), 0, stream, r, kScanTotal);
+      launch_scan(r, kScanTotal, stream);
     }
     if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
     {

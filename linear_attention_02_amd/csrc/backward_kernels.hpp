@@ -55,6 +55,8 @@ struct BwdParams {
   int recR;
   f32x2 *stats;       // [heads][stats_stride] pairs (1/den_i, b_i)
   long long stats_stride;
+  int sum_in_walk;    // causal: wsF, wsR hold segment totals; each walk sums
+                      // its own prefix (suffix) from them
 };
 
 // Row tiles per chunk of the causal backward walks (32-token chunks): the
@@ -303,10 +305,11 @@ template <class E> __device__ inline void bwd_walk_f(const BwdParams &p) {
   constexpr int kT = 16 * NT;
 
   State st;
-  if (p.recF > 0) {
+  if (p.recF > 0 && !p.sum_in_walk) {
     state_load_record(st, p.wsF + ((long long)h * p.recF + s) * kStateFloats, lane, g);
   } else {
     state_zero(st);
+    if (p.recF > 0) state_add_records(st, p.wsF + (long long)h * p.recF * kStateFloats, s, kStateFloats, lane, g);
   }
   if constexpr (std::is_same<E, __bf16>::value) {
     __shared__ u32x4 slot[Slot<4, NT>::kVec];
@@ -639,10 +642,13 @@ template <class E> __device__ inline void bwd_walk_r(const BwdParams &p) {
   const long long last = t_begin + ((t_end - 1 - t_begin) / kT) * kT;
 
   State rs;
-  if (p.recR > 0) {
+  if (p.recR > 0 && !p.sum_in_walk) {
     state_load_record(rs, p.wsR + ((long long)h * p.recR + s) * kStateFloats, lane, g);
   } else {
     state_zero(rs);
+    if (p.recR > 0)
+      state_add_records(rs, p.wsR + ((long long)h * p.recR + p.segments - 1) * kStateFloats, p.segments - 1 - s,
+                        -(long long)kStateFloats, lane, g);
   }
   if constexpr (std::is_same<E, __bf16>::value) {
     __shared__ u32x4 slot[Slot<4, NT>::kVec + 8 * NT];

@@ -41,7 +41,9 @@ namespace linattn {
 // z: [ct 4][g 4][r 4] = 64 floats, z[pi(ct,g,r)].
 constexpr int kStateFloats = 4096 + 64;
 
-enum InitMode : int { kInitZero = 0, kInitRecord = 1, kInitNatural = 2 };
+// kInitTotals: the workspace holds segment totals (no scan ran); the walk
+// sums its own prefix from them, seeded with S0, z0 when given.
+enum InitMode : int { kInitZero = 0, kInitRecord = 1, kInitNatural = 2, kInitTotals = 3 };
 
 struct FwdParams {
   const void *Q, *K, *V;
@@ -53,7 +55,7 @@ struct FwdParams {
   float *ws;           // [heads][records][kStateFloats]
   int records;         // records per head in ws
   int init;            // InitMode for the walk kernel
-  const float *S0;     // natural order [heads][64][64] (kInitNatural / scan seed)
+  const float *S0;     // natural order [heads][64][64] (kInitNatural, kInitTotals / scan seed)
   const float *z0;     // [heads][64]
   float *S_out;        // natural order final state, written by the last segment
   float *z_out;
@@ -481,7 +483,8 @@ __global__ __launch_bounds__(64, 1) void seg_totals_kernel(FwdParams p, int tota
 }
 
 // ---------------------------------------------------------------------------
-// Scan over segment records, one thread per (head, state element).
+// Scan over segment records, one thread per (head, W consecutive state
+// elements).
 //   causal:     records 0..P-2 hold totals -> become exclusive prefixes seeded
 //               with S0/z0 (or zero); record P-1 receives the prefix of the
 //               last segment.
@@ -490,44 +493,63 @@ __global__ __launch_bounds__(64, 1) void seg_totals_kernel(FwdParams p, int tota
 //               the later segments); record 0 receives the suffix of segment 0.
 //   non-causal: record P receives the sum of records 0..P-1.
 // The loads do not depend on the running sum, so they are issued in batches
-// (one memory latency per batch) before the dependent stores.  The order of
-// additions is fixed, so results are deterministic.
+// (one memory latency per batch) before the dependent stores.  Every element
+// is summed in record order, so results are deterministic and do not depend
+// on W or the batch.  The host picks W = 4 (wide accesses) when that still
+// gives a launch of at least 256 blocks, else W = 1, and a batch of eight for
+// up to eight records (fewer registers, more resident waves).
 // ---------------------------------------------------------------------------
-constexpr int kScanBatch = 32;
+constexpr int kScanBatchSmall = 8;
+constexpr int kScanBatchLarge = 32;
+static_assert(kStateFloats % 4 == 0, "state records split into whole vectors");
 
 enum ScanMode : int { kScanTotal = 0, kScanPrefix = 1, kScanSuffix = 2 };
 
+template <int W> struct ScanVecType;
+template <> struct ScanVecType<1> { typedef float type; };
+template <> struct ScanVecType<4> { typedef f32x4 type; };
+
+// Element e of a head's record, from the natural-order S0, z0 (record layout:
+// S tiles [ct][mt][lane][r], then z [ct][g][r]).
+__device__ inline float scan_seed(const FwdParams &p, int h, int e) {
+  if (e < 4096) {
+    const int ct = e >> 10, mt = (e >> 8) & 3, lane = (e >> 2) & 63, r = e & 3;
+    const int c = pi_col(ct, lane >> 4, r);
+    const int m = pi_col(mt, (lane & 15) >> 2, lane & 3);
+    return p.S0[(long long)h * 4096 + c * 64 + m];
+  }
+  const int f = e - 4096;
+  const int ct = f >> 4, g = (f >> 2) & 3, r = f & 3;
+  return p.z0[(long long)h * 64 + pi_col(ct, g, r)];
+}
+
+template <int W, int kBatch>
 __global__ __launch_bounds__(256) void scan_kernel(FwdParams p, int mode) {
+  typedef typename ScanVecType<W>::type V;
+  constexpr int kThreads = kStateFloats / W;  // per head
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const int h = (int)(idx / kStateFloats);
-  const int e = (int)(idx % kStateFloats);
+  const int h = (int)(idx / kThreads);
+  const int e0 = (int)(idx % kThreads) * W;
   if (h >= p.heads) return;
   const int P = p.segments;
   // Logical record s lives at position s (prefix) or P - 1 - s (suffix).
-  const long long step = mode == kScanSuffix ? -(long long)kStateFloats : (long long)kStateFloats;
-  float *recs = p.ws + (long long)h * p.records * kStateFloats + e +
-                (mode == kScanSuffix ? (long long)(P - 1) * kStateFloats : 0);
+  const long long step = (mode == kScanSuffix ? -(long long)kStateFloats : (long long)kStateFloats) / W;
+  V *recs = reinterpret_cast<V *>(p.ws + (long long)h * p.records * kStateFloats + e0 +
+                                  (mode == kScanSuffix ? (long long)(P - 1) * kStateFloats : 0));
   if (mode != kScanTotal) {
-    float run = 0.f;
+    V run = V{};
     if (mode == kScanPrefix && p.S0 != nullptr) {
-      if (e < 4096) {
-        const int ct = e >> 10, mt = (e >> 8) & 3, lane = (e >> 2) & 63, r = e & 3;
-        const int c = pi_col(ct, lane >> 4, r);
-        const int m = pi_col(mt, (lane & 15) >> 2, lane & 3);
-        run = p.S0[(long long)h * 4096 + c * 64 + m];
-      } else {
-        const int f = e - 4096;
-        const int ct = f >> 4, g = (f >> 2) & 3, r = f & 3;
-        run = p.z0[(long long)h * 64 + pi_col(ct, g, r)];
-      }
-    }
-    for (int s0 = 0; s0 + 1 < P; s0 += kScanBatch) {
-      float t[kScanBatch];
+      float *run_e = reinterpret_cast<float *>(&run);
 #pragma unroll
-      for (int u = 0; u < kScanBatch; ++u)
+      for (int r = 0; r < W; ++r) run_e[r] = scan_seed(p, h, e0 + r);
+    }
+    for (int s0 = 0; s0 + 1 < P; s0 += kBatch) {
+      V t[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
         if (s0 + u + 1 < P) t[u] = recs[(long long)(s0 + u) * step];
 #pragma unroll
-      for (int u = 0; u < kScanBatch; ++u)
+      for (int u = 0; u < kBatch; ++u)
         if (s0 + u + 1 < P) {
           recs[(long long)(s0 + u) * step] = run;
           run += t[u];
@@ -535,15 +557,53 @@ __global__ __launch_bounds__(256) void scan_kernel(FwdParams p, int mode) {
     }
     recs[(long long)(P - 1) * step] = run;
   } else {
-    float run = 0.f;
-    for (int s0 = 0; s0 < P; s0 += kScanBatch) {
-      float t[kScanBatch];
+    V run = V{};
+    for (int s0 = 0; s0 < P; s0 += kBatch) {
+      V t[kBatch];
 #pragma unroll
-      for (int u = 0; u < kScanBatch; ++u) t[u] = s0 + u < P ? recs[(long long)(s0 + u) * kStateFloats] : 0.f;
+      for (int u = 0; u < kBatch; ++u) t[u] = s0 + u < P ? recs[(long long)(s0 + u) * step] : V{};
 #pragma unroll
-      for (int u = 0; u < kScanBatch; ++u) run += t[u];
+      for (int u = 0; u < kBatch; ++u) run += t[u];
     }
-    recs[(long long)P * kStateFloats] = run;
+    recs[(long long)P * step] = run;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefix of segment s summed by its own walk wave: st (the seed S0, z0 or
+// zero) += totals records 0..s-1, in record order -- the same additions, in
+// the same order, as the prefix scan, so the state is bit-identical (the
+// backward's reverse walk sums the later segments' records the same way,
+// last first, as the suffix scan does).  Used for few segments per head,
+// where it costs less than a scan launch; two records are loaded before they
+// are added.
+// ---------------------------------------------------------------------------
+constexpr int kSumInWalkMaxSegments = 8;
+
+__device__ inline void state_add(State &st, const State &t) {
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    st.z[a] += t.z[a];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) st.S[a][b] += t.S[a][b];
+  }
+}
+
+// st += records first, first + stride, ... (count of them, in that order).
+__device__ inline void state_add_records(State &st, const float *first, int count, long long stride, int lane,
+                                         int g) {
+  int j = 0;
+  for (; j + 2 <= count; j += 2) {
+    State a, b;
+    state_load_record(a, first + j * stride, lane, g);
+    state_load_record(b, first + (j + 1) * stride, lane, g);
+    state_add(st, a);
+    state_add(st, b);
+  }
+  if (j < count) {
+    State a;
+    state_load_record(a, first + j * stride, lane, g);
+    state_add(st, a);
   }
 }
 
@@ -661,20 +721,27 @@ __device__ inline void causal_walk(const FwdParams &p) {
   const Frag<E> ident = frag_identity<E>(n16, g);
 
   State st;
-  if (p.init == kInitRecord) {
-    state_load_record(st, p.ws + ((long long)h * p.records + s) * kStateFloats, lane, g);
-  } else if (p.init == kInitNatural) {
-    state_load_natural(st, p.S0 + (long long)h * 4096, p.z0 + (long long)h * 64, n16, g);
-  } else {
-    state_zero(st);
-  }
+  auto init_state = [&]() {
+    if (p.init == kInitRecord) {
+      state_load_record(st, p.ws + ((long long)h * p.records + s) * kStateFloats, lane, g);
+    } else if (p.init == kInitNatural || (p.init == kInitTotals && p.S0 != nullptr)) {
+      state_load_natural(st, p.S0 + (long long)h * 4096, p.z0 + (long long)h * 64, n16, g);
+    } else {
+      state_zero(st);
+    }
+    if (p.init == kInitTotals)
+      state_add_records(st, p.ws + (long long)h * p.records * kStateFloats, s, kStateFloats, lane, g);
+  };
 
   if constexpr (std::is_same<E, __bf16>::value) {
     constexpr int NT = kWalkTilesBf16;
     constexpr int kT = 16 * NT;
     __shared__ u32x4 slot[Slot<3, NT>::kVec];
     const __bf16 *src[3] = {Qh, Kh, Vh};
+    // The first chunk's loads go out before the state's, so that their
+    // latencies overlap.
     if (t_begin < t_end) stage_issue<3, NT>(slot, src, t_begin, (int)min<long long>(kT, t_end - t_begin), n16, g);
+    init_state();
     for (long long t0 = t_begin; t0 < t_end; t0 += kT) {
       const int rows = (int)min<long long>(kT, t_end - t0);
       // Outstanding vector-memory operations: this chunk's loads, then the
@@ -692,6 +759,7 @@ __device__ inline void causal_walk(const FwdParams &p) {
       }
     }
   } else {
+    init_state();
     const E *src[3] = {Qh, Kh, Vh};
     for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
       const int rows = chunk_rows(t0, t_end);

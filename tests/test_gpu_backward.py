@@ -142,7 +142,7 @@ def test_named_workload_backward_full_size(name):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("segments", [0, 5])
+@pytest.mark.parametrize("segments", [0, 5, 12])  # 12: records hold scanned prefixes
 def test_backward_after_forward_is_bitwise_identical(dtype, causal, segments):
     # Reusing the segment states the forward left in the workspace gives the
     # same bits as recomputing them.

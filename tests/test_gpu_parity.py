@@ -95,7 +95,9 @@ def test_heads_are_independent():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("segments", [1, 4])
+# 4 segments: each walk sums the earlier segments' totals itself; 12 (11 for
+# the 652-token part): the prefix scan, seeded with the carried state.
+@pytest.mark.parametrize("segments", [1, 4, 12])
 def test_forward_state_split_and_resume(dtype, segments):
     la.set_segments(segments)
     q, k, v = draw_qkv(2, 2, 1100, 64, 64, dtype, seed=21)
