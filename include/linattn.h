@@ -17,7 +17,9 @@
  *
  * Conventions shared by every entry point:
  *   - Pointers are device pointers (hipMalloc / PyTorch CUDA tensors) unless a
- *     comment says otherwise; all must be 16-byte aligned.
+ *     comment says otherwise; all must be 16-byte aligned.  Kernels run on
+ *     the calling thread's current HIP device: the buffers and `stream` must
+ *     belong to it (this is not checked).
  *   - Tensors are contiguous row-major.  Q, K: [B, H, N, C]; V, O: [B, H, N, M].
  *   - This version supports C = M = 64 only (other values: LINATTN_ERR_SHAPE).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are
@@ -28,7 +30,8 @@
  *   - The library allocates no device memory and keeps none between calls.
  *     Scratch space is the caller's `workspace`.
  *   - The library is reentrant.  Its only global state is a per-thread error
- *     message, a per-device attribute cache and the optional kernel timer.
+ *     message, a per-device attribute cache, the segment-count override of
+ *     linattn_set_segments and the optional kernel timer.
  *   - No C++ exception crosses this interface.
  */
 #ifndef LINATTN_H

@@ -9,9 +9,13 @@ present, calls raise.
 
     forward(q, k, v, causal=True)               -> o
     forward_state(q, k, v, S0=None, z0=None)    -> (o, S_N, z_N)   causal, carries state
+    backward(q, k, v, grad_out, causal=True)    -> (dq, dk, dv)
     decode_step(S, z, q, k, v)                  -> o               updates S, z in place
+    decode_step_strided(S, z, q, k, v)          -> o               q, k, v as strided row views
 
 q, k: [B, H, N, 64]; v: [B, H, N, 64]; float32 or bfloat16, contiguous, CUDA.
+Each call runs on the device of its tensors, on that device's current stream
+unless ``stream`` is given.
 """
 from __future__ import annotations
 
@@ -20,8 +24,9 @@ import os
 import re
 from typing import Optional, Tuple
 
-__all__ = ["forward", "forward_state", "decode_step", "workspace_bytes", "state_workspace_bytes", "lib",
-           "LinattnError", "timer", "set_segments", "plan_segments", "LIB_PATH", "HEADER_PATH"]
+__all__ = ["forward", "forward_state", "backward", "decode_step", "decode_step_strided", "workspace_bytes",
+           "state_workspace_bytes", "backward_workspace_bytes", "lib", "LinattnError", "timer", "set_segments",
+           "plan_segments", "LIB_PATH", "HEADER_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblinattn.so")
@@ -130,11 +135,18 @@ def _check_cuda(*ts):
             raise LinattnError(8, "tensors must be contiguous")
 
 
-def _stream(stream) -> int:
+def _stream(stream, device) -> int:
     torch = _torch()
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _call(device, fn, *args):
+    """Calls a library entry point with ``device`` as the current HIP device
+    (the library launches on the current device) and raises on an error status."""
+    with _torch().cuda.device(device):
+        _raise(fn(*args))
 
 
 def _ptr(t) -> Optional[int]:
@@ -182,9 +194,8 @@ def forward(q, k, v, causal: bool = True, out=None, workspace=None, stream=None)
         out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
     nbytes = int(lib().linattn_forward_workspace_bytes(B, H, N, C, M, dt, int(bool(causal))))
     ws = _alloc_ws(nbytes, q.device, workspace)
-    rc = lib().linattn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, C, M, dt, int(bool(causal)),
-                               _ptr(ws), nbytes, _stream(stream))
-    _raise(rc)
+    _call(q.device, lib().linattn_forward, _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, C, M, dt,
+          int(bool(causal)), _ptr(ws), nbytes, _stream(stream, q.device))
     return out
 
 
@@ -208,9 +219,8 @@ def forward_state(q, k, v, S0=None, z0=None, out=None, S_out=None, z_out=None, w
             raise LinattnError(3, "states are float32")
     nbytes = int(lib().linattn_forward_state_workspace_bytes(B, H, N, C, M, dt))
     ws = _alloc_ws(nbytes, q.device, workspace)
-    rc = lib().linattn_forward_state(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, C, M, dt, _ptr(S0), _ptr(z0),
-                                     _ptr(S_out), _ptr(z_out), _ptr(ws), nbytes, _stream(stream))
-    _raise(rc)
+    _call(q.device, lib().linattn_forward_state, _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, C, M, dt, _ptr(S0),
+          _ptr(z0), _ptr(S_out), _ptr(z_out), _ptr(ws), nbytes, _stream(stream, q.device))
     return out, S_out, z_out
 
 
@@ -224,8 +234,8 @@ def backward(q, k, v, grad_out, causal: bool = True, dq=None, dk=None, dv=None, 
     """Gradients of ``forward`` (zero initial state) for dL/dO = grad_out; returns (dq, dk, dv).
 
     after_forward=True: ``workspace`` (sized by backward_workspace_bytes) was last
-    written by ``forward`` on the same q, k, v and causal flag, and its segment
-    states are reused instead of recomputed.
+    written by ``forward`` on the same q, k, v and causal flag, and the segment
+    records it holds are reused instead of recomputed.
     """
     torch = _torch()
     _check_cuda(q, k, v, grad_out, dq, dk, dv)
@@ -241,9 +251,8 @@ def backward(q, k, v, grad_out, causal: bool = True, dq=None, dk=None, dv=None, 
         raise LinattnError(8, "after_forward needs the workspace the forward used")
     ws = _alloc_ws(nbytes, q.device, workspace)
     fn = lib().linattn_backward_after_forward if after_forward else lib().linattn_backward
-    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(grad_out), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, C, M, dt,
-            int(bool(causal)), _ptr(ws), nbytes, _stream(stream))
-    _raise(rc)
+    _call(q.device, fn, _ptr(q), _ptr(k), _ptr(v), _ptr(grad_out), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, C, M, dt,
+          int(bool(causal)), _ptr(ws), nbytes, _stream(stream, q.device))
     return dq, dk, dv
 
 
@@ -266,9 +275,8 @@ def decode_step(S, z, q, k, v, out=None, stream=None):
     dt = _dt(q)
     if out is None:
         out = torch.empty((BH, M), dtype=torch.float32, device=q.device)
-    rc = lib().linattn_decode_step(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), BH, C, M, dt,
-                                   _stream(stream))
-    _raise(rc)
+    _call(q.device, lib().linattn_decode_step, _ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), BH, C, M, dt,
+          _stream(stream, q.device))
     return out
 
 
@@ -332,7 +340,6 @@ def decode_step_strided(S, z, q, k, v, out=None, stream=None):
         raise LinattnError(2, "decode_step_strided shape mismatch")
     if out is None:
         out = torch.empty((BH, M), dtype=torch.float32, device=q.device)
-    rc = lib().linattn_decode_step_strided(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), BH, C, M,
-                                           _dt(q), int(stride), _stream(stream))
-    _raise(rc)
+    _call(q.device, lib().linattn_decode_step_strided, _ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), BH,
+          C, M, _dt(q), int(stride), _stream(stream, q.device))
     return out

@@ -78,6 +78,10 @@ struct TimerScope {
       return;
     }
     active = hipEventRecord(ev.start, stream) == hipSuccess;
+    if (!active) {
+      (void)hipEventDestroy(ev.start);
+      (void)hipEventDestroy(ev.stop);
+    }
   }
   ~TimerScope() {
     if (!active) return;

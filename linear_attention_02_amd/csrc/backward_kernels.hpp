@@ -27,6 +27,8 @@
 // and the per-token pair (1/den_i, b_i); a totals pass over Q, dO and those
 // pairs gives each segment's sum of phi(q) a^T and b phi(q); the scan run in
 // reverse turns them into suffix states; a right-to-left walk writes dK, dV.
+// With at most eight segments per head neither scan runs: each walk wave sums
+// the totals records it needs itself, in the scan's order.
 // Non-causal: S, z are the head's totals; one read pass writes dQ, the pairs
 // and per-range partial sums of R, r; a scan totals those; a second read pass
 // writes dK and dV.  All products are 16x16 MFMA tiles in the layouts of

@@ -24,8 +24,9 @@
 // the grid wide enough for few-head workloads; their starting states come
 // from a two-pass scan (segment totals, then an exclusive prefix per head),
 // the parallel-scan resolution of the left-to-right dependency ("Why Replace
-// Attention?", §7.7).  No LDS and no inter-wave synchronisation: every wave
-// is independent, data is exchanged only through the scan's workspace.
+// Attention?", §7.7).  No inter-wave synchronisation: each wave's LDS is a
+// private staging slot, and waves exchange data only through the workspace
+// records, between kernel launches.
 #pragma once
 
 #include <type_traits>
@@ -253,9 +254,12 @@ __device__ inline Frag<__bf16> lds_tok_frag(const u32x4 *slot, int tsr, int jt, 
   return f;
 }
 
-// Walks the chunks [t_begin, t_end): body(slot, t0, rows) runs on each chunk
-// while the next one streams into the slot.  kStores is the number of
-// vector-memory stores body() issues on a full chunk.
+// Walks the chunks [t_begin, t_end), the first one prefetched here.
+// body(slot, t0, rows) runs on each chunk once its loads have landed: it reads
+// the slot into registers, waits for lgkmcnt(0), issues the next chunk's loads
+// into the same slot and then computes, so one chunk streams in while one is
+// computed.  kStores is the number of vector-memory stores body() issues on a
+// full chunk.
 template <int kTensors, int kStores, int kPolicy, class Body>
 __device__ inline void stream_lds(u32x4 *slot, const __bf16 *const src[kTensors], long long t_begin, long long t_end,
                                   int n16, int g, Body &&body) {
@@ -272,9 +276,7 @@ __device__ inline void stream_lds(u32x4 *slot, const __bf16 *const src[kTensors]
     } else {
       wait_vmcnt<kStores>();
     }
-    body(slot, t0, rows);  // reads the slot into registers first, then waits for lgkmcnt(0)
-    const long long t1 = t0 + kChunk;
-    (void)t1;
+    body(slot, t0, rows);
   }
 }
 
@@ -430,7 +432,6 @@ __global__ __launch_bounds__(64, 1) void seg_totals_kernel(FwdParams p, int tota
     __shared__ u32x4 slot[Slot<2>::kVec];
     const __bf16 *src[2] = {Kh, Vh};
     stream_lds<2, 0, kPolicy>(slot, src, t_begin, t_end, n16, g, [&](const u32x4 *sl, long long t0, int rows) {
-      (void)t0;
       Frag<E> kt[4][4], vt[4][4];
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt)
