@@ -69,6 +69,29 @@ def read_counters(kernel: str, workload: str):
         return None
 
 
+def measured_copy_peak(torch) -> dict:
+    """Bandwidth of a plain 1 GiB device-to-device copy on this GPU (read + write
+    bytes over time, median of 10), the practical ceiling the forward's HBM
+    fraction is also compared with."""
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    times = []
+    for _ in range(10):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        b.copy_(a)
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    ms = sorted(times)[len(times) // 2]
+    del a, b
+    return {"GBs": 2 * 4 * n / (ms * 1e-3) / 1e9, "bytes_moved": 2 * 4 * n, "median_ms": ms,
+            "what": "torch copy_ of 1 GiB fp32 on the device, read + write bytes"}
+
+
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -456,6 +479,11 @@ def main():
     }
     log(f"forward {w.name}: cold-cache calls")
     result["forward_call"]["cold"] = time_forward_cold(la, torch, w)
+    log("measured copy peak")
+    copy_peak = measured_copy_peak(torch)
+    result["hbm_measured_copy"] = copy_peak
+    result["roofline"]["frac_of_measured_copy"] = achieved / copy_peak["GBs"]
+    result["forward_call"]["frac_of_measured_copy"] = result["forward_call"]["achieved_GBs"] / copy_peak["GBs"]
     if not args.no_noncausal:
         for key, name in (("causal_cifar_shaped", "causal_bf16_b16h8n3072"), ("noncausal", "noncausal_bf16_b8h8n4096")):
             wn = WORKLOADS[name]
