@@ -15,7 +15,8 @@ present, calls raise.
 
 q, k: [B, H, N, 64]; v: [B, H, N, 64]; float32 or bfloat16, contiguous, CUDA.
 Each call runs on the device of its tensors, on that device's current stream
-unless ``stream`` is given.
+unless ``stream`` is given.  ``linear_attention_02_amd.autograd.linear_attention``
+wraps forward and backward as a torch.autograd.Function.
 """
 from __future__ import annotations
 
