@@ -311,6 +311,8 @@ def sequence_sweep(la, torch, steps, warmup, B=1, H=8, exps=range(9, 17)):
             la.backward(q, k, v, g, causal=True, dq=dq, dk=dk, dv=dv, workspace=bwd_ws)
 
         res = {"N": N}
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
         for key, fn in (("fwd_ms", fwd), ("fwd_bwd_ms", fwd_bwd)):
             for _ in range(warmup):
                 fn()
@@ -321,14 +323,32 @@ def sequence_sweep(la, torch, steps, warmup, B=1, H=8, exps=range(9, 17)):
                 fn()
             end.record()
             torch.cuda.synchronize()
+            res[key + "_eager"] = start.elapsed_time(end) / steps
+            # The same `steps` calls captured in one HIP graph and replayed
+            # once: device time without the Python binding's per-call host
+            # overhead, which the eager loop pays at small N.
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=side):
+                for _ in range(steps):
+                    fn()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            start.record()
+            graph.replay()
+            end.record()
+            torch.cuda.synchronize()
             res[key] = start.elapsed_time(end) / steps
+            del graph
         res["peak_bytes_fwd_bwd"] = int(peak)
         res["input_bytes"] = int(4 * q.numel() * 2)
         rows.append(res)
         del q, k, v, g, o, dq, dk, dv, fwd_ws, bwd_ws
     return {"shape": f"causal bf16 B={B} H={H} C=M=64", "rows": rows,
             "peak_note": "device memory allocated during one forward + backward call beyond the inputs "
-                         "(O, dQ, dK, dV and both workspaces)"}
+                         "(O, dQ, dK, dV and both workspaces)",
+            "time_note": "fwd_ms, fwd_bwd_ms: one replay of a HIP graph holding the timed calls, per call "
+                         "(device time); *_eager: a loop of Python calls"}
 
 
 def time_generation(torch, cfg, dtype):

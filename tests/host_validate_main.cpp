@@ -28,7 +28,19 @@ int main() {
   EXPECT(p.segments == 8 && p.seg_chunks == 6);
   p = plan_forward(64, 4096, 0, 256, 0);
   EXPECT(p.segments == 16 && p.records == 17 && p.ranges == 16 && p.range_chunks == 4);
-  p = plan_forward(1, 65, 1, 256, 0);  // two chunks, cannot split below 4 chunks per segment
+  // Few heads, short sequences: segments shorter than 4 chunks (down to one)
+  // where longer ones would leave the device short of waves, at most 64.
+  p = plan_forward(1, 65, 1, 256, 0);  // two chunks
+  EXPECT(p.segments == 2 && p.seg_chunks == 1 && p.records == 2 && p.workspace_bytes == (size_t)2 * 4160 * 4);
+  p = plan_forward(8, 512, 1, 256, 0);
+  EXPECT(p.segments == 8 && p.seg_chunks == 1);
+  p = plan_forward(8, 8192, 1, 256, 0);
+  EXPECT(p.segments == 64 && p.seg_chunks == 2);
+  p = plan_forward(8, 16384, 1, 256, 0);  // 4-chunk segments already fill the device
+  EXPECT(p.segments == 64 && p.seg_chunks == 4);
+  p = plan_forward(1, 1 << 20, 1, 256, 0);
+  EXPECT(p.segments == 1024 && p.seg_chunks == 16);
+  p = plan_forward(1, 64, 1, 256, 0);  // one chunk: one segment, no records
   EXPECT(p.segments == 1 && p.records == 0 && p.workspace_bytes == 0);
   p = plan_forward(1, 64 * 10, 1, 256, 4);  // override
   EXPECT(p.segments == 4 && p.seg_chunks == 3);

@@ -21,7 +21,7 @@ def _reset_segments():
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("segments", [0, 14])
+@pytest.mark.parametrize("segments", [0, 5])  # 0: 14 one-chunk segments (scans); 5: in-walk prefixes
 def test_autograd_matches_library_backward(segments, causal, dtype):
     la.set_segments(segments)
     B, H, N = 1, 2, 64 * 13 + 7
