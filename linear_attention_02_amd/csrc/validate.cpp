@@ -81,6 +81,7 @@ Plan plan_forward(long long heads, long long N, int causal, int cus, int overrid
   if (segs > p.chunks) segs = p.chunks;
   if (segs < 1) segs = 1;
   if (segs > INT_MAX / 2) segs = INT_MAX / 2;
+  if (segs > 1 && heads * segs > INT_MAX) segs = std::max(1LL, (long long)INT_MAX / heads);  // grid size
   long long seg_chunks = ceil_div(p.chunks, segs);
   segs = ceil_div(p.chunks, seg_chunks);  // no empty segment
   p.segments = (int)segs;

@@ -1,5 +1,6 @@
 // Host-only driver for validate.cpp: exercises the argument checks and the
 // planner without HIP, so they can run under AddressSanitizer and UBSan.
+#include <climits>
 #include <cstdio>
 #include <cstdlib>
 
@@ -42,6 +43,8 @@ int main() {
   EXPECT(p.segments == 1024 && p.seg_chunks == 16);
   p = plan_forward(1, 64, 1, 256, 0);  // one chunk: one segment, no records
   EXPECT(p.segments == 1 && p.records == 0 && p.workspace_bytes == 0);
+  p = plan_forward(1 << 24, 64 * 1000, 1, 256, 1000);  // override: the grid stays within INT_MAX waves
+  EXPECT((long long)p.segments * (1 << 24) <= INT_MAX && p.segments >= 1);
   p = plan_forward(1, 64 * 10, 1, 256, 4);  // override
   EXPECT(p.segments == 4 && p.seg_chunks == 3);
   p = plan_forward(1, 64 * 10, 1, 256, 1000);  // override capped at the chunk count
