@@ -71,6 +71,14 @@ def test_segment_count_does_not_change_results(segments, dtype):
     check_backward(q, k, v, g, False, dtype, label=f"segments={segments} noncausal")
 
 
+@pytest.mark.parametrize("N", [512, 4096, 8192])  # the planner's short-segment regime
+def test_sequence_sweep_shapes(N):
+    q, k, v = draw_qkv(1, 8, N, 64, 64, "bf16", seed=5000 + N)
+    g = draw_grad_output(1, 8, N, 64, "bf16", 5000 + N)
+    note(f"[grad] sweep shape N={N} segments={la.plan_segments(1, 8, N, torch.bfloat16, True)}")
+    check_backward(q, k, v, g, True, "bf16", label=f"sweep B1H8N{N}")
+
+
 def test_mixed_scales():
     gen = torch.Generator().manual_seed(55)
     q = (torch.randn(1, 2, 700, 64, generator=gen) * 3).to(torch.bfloat16)

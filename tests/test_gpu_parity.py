@@ -43,6 +43,16 @@ def test_segment_count_does_not_change_results(segments, dtype):
     check_forward(q, k, v, False, dtype, label=f"segments={segments} noncausal")
 
 
+# The planner's short-segment regime (few heads, N up to 16K): one-chunk
+# segments with in-walk prefixes (N = 512: 8 segments), one-chunk segments with
+# the scan (N = 4096: 64), two-chunk segments with the scan (N = 8192: 64).
+@pytest.mark.parametrize("N", [512, 4096, 8192])
+def test_sequence_sweep_shapes(N):
+    q, k, v = draw_qkv(1, 8, N, 64, 64, "bf16", seed=4000 + N)
+    note(f"[parity] sweep shape N={N} segments={la.plan_segments(1, 8, N, torch.bfloat16, True)}")
+    check_forward(q, k, v, True, "bf16", label=f"sweep B1H8N{N}")
+
+
 def test_mixed_scales_and_large_magnitudes():
     # Inputs far from N(0, 1): both phi branches, large positive features.
     g = torch.Generator().manual_seed(5)
