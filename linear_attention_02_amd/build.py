@@ -19,8 +19,8 @@ LIB = os.path.join(HERE, "liblinattn.so")
 ARCH = os.environ.get("LINATTN_ARCH", "gfx950")
 
 SOURCES = [os.path.join(CSRC, "api.hip"), os.path.join(CSRC, "validate.cpp")]
-HEADERS = [os.path.join(CSRC, f) for f in ("device_common.hpp", "forward_kernels.hpp", "decode_kernel.hpp",
-                                            "validate.hpp")] + [os.path.join(ROOT, "include", "linattn.h")]
+HEADERS = [os.path.join(CSRC, f) for f in ("device_common.hpp", "forward_kernels.hpp", "backward_kernels.hpp",
+                                            "decode_kernel.hpp", "validate.hpp")] + [os.path.join(ROOT, "include", "linattn.h")]
 
 # Packed-fp32 VALU instructions are kept out of the generated code.
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
