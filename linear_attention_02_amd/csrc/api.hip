@@ -117,7 +117,16 @@ template <class E> TotalsKernel<E> totals_kernel(long long heads, long long N) {
 
 // One thread per (head, W state elements): W = 4 while that still launches
 // 256 blocks or more, else 1; a batch of eight loads for up to eight records.
+// More than kScanGroupedFrom records per head go to the grouped scan instead.
+constexpr int kScanGroupedFrom = 128;
+
 void launch_scan(const FwdParams &p, int mode, hipStream_t stream) {
+  const int cnt = mode == kScanTotal ? p.segments : p.segments - 1;
+  if (cnt >= kScanGroupedFrom && (long long)p.heads * kScanBlocksPerHead <= INT_MAX) {
+    const unsigned blocks = (unsigned)((long long)p.heads * kScanBlocksPerHead);
+    hipLaunchKernelGGL(scan_grouped_kernel, dim3(blocks), dim3(256), 0, stream, p, mode);
+    return;
+  }
   const long long blocks4 = ((long long)p.heads * (kStateFloats / 4) + 255) / 256;
   const long long blocks1 = ((long long)p.heads * kStateFloats + 255) / 256;
   const bool small = p.segments <= kScanBatchSmall;

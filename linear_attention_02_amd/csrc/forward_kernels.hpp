@@ -571,6 +571,85 @@ __global__ __launch_bounds__(256) void scan_kernel(FwdParams p, int mode) {
 }
 
 // ---------------------------------------------------------------------------
+// The same scans for many records per head (few heads, very long sequences),
+// where one thread per element would walk hundreds of records one batch after
+// another.  A block covers kScanVecs four-element vectors of one head's
+// records with kScanGroups groups of threads; group g owns a run of `per`
+// consecutive records.  Each thread sums its run, the run totals meet in LDS,
+// and each thread then writes its records' prefixes starting from the sum of
+// the earlier runs.  Additions run in a fixed order (runs in record order,
+// records in order within a run), so results are deterministic.
+// ---------------------------------------------------------------------------
+constexpr int kScanGroups = 32;
+constexpr int kScanVecs = 256 / kScanGroups;
+constexpr int kScanRunBatch = 32;  // records of a run loaded at once
+constexpr int kScanBlocksPerHead = (kStateFloats / 4 + kScanVecs - 1) / kScanVecs;
+
+__global__ __launch_bounds__(256) void scan_grouped_kernel(FwdParams p, int mode) {
+  const long long hb = blockIdx.x;
+  const int h = (int)(hb / kScanBlocksPerHead);
+  const int vb = (int)(hb % kScanBlocksPerHead);
+  const int grp = threadIdx.x / kScanVecs, lv = threadIdx.x % kScanVecs;
+  const int e4 = vb * kScanVecs + lv;
+  const bool active = e4 < kStateFloats / 4;
+  const int P = p.segments;
+  const int cnt = mode == kScanTotal ? P : P - 1;  // records summed
+  const int per = (cnt + kScanGroups - 1) / kScanGroups;
+  const int j0 = min(cnt, grp * per), j1 = min(cnt, j0 + per);
+  // Logical record j lives at position j (prefix, total) or P - 1 - j (suffix).
+  const long long step = (mode == kScanSuffix ? -(long long)kStateFloats : (long long)kStateFloats) / 4;
+  f32x4 *recs = reinterpret_cast<f32x4 *>(p.ws + (long long)h * p.records * kStateFloats +
+                                          (mode == kScanSuffix ? (long long)(P - 1) * kStateFloats : 0)) +
+                e4;
+  __shared__ f32x4 run_total[kScanGroups][kScanVecs];
+  f32x4 t[kScanRunBatch];
+  f32x4 local = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (active) {
+    for (int b = j0; b < j1; b += kScanRunBatch) {
+#pragma unroll
+      for (int u = 0; u < kScanRunBatch; ++u)
+        if (b + u < j1) t[u] = recs[(long long)(b + u) * step];
+#pragma unroll
+      for (int u = 0; u < kScanRunBatch; ++u)
+        if (b + u < j1) local += t[u];
+    }
+  }
+  run_total[grp][lv] = local;
+  __syncthreads();
+  if (!active) return;
+  if (mode == kScanTotal) {
+    if (grp == 0) {
+      f32x4 run = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int g2 = 0; g2 < kScanGroups; ++g2) run += run_total[g2][lv];
+      recs[(long long)P * step] = run;
+    }
+    return;
+  }
+  f32x4 run = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (mode == kScanPrefix && p.S0 != nullptr) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) run[r] = scan_seed(p, h, 4 * e4 + r);
+  }
+  for (int g2 = 0; g2 < grp; ++g2) run += run_total[g2][lv];
+  // The run's records are read again unless they are all still held in t.
+  const bool held = j1 - j0 <= kScanRunBatch;
+  for (int b = j0; b < j1; b += kScanRunBatch) {
+    if (!held) {
+#pragma unroll
+      for (int u = 0; u < kScanRunBatch; ++u)
+        if (b + u < j1) t[u] = recs[(long long)(b + u) * step];
+    }
+#pragma unroll
+    for (int u = 0; u < kScanRunBatch; ++u)
+      if (b + u < j1) {
+        recs[(long long)(b + u) * step] = run;
+        run += t[u];
+      }
+  }
+  if (j0 < j1 && j1 == cnt) recs[(long long)cnt * step] = run;
+}
+
+// ---------------------------------------------------------------------------
 // Prefix of segment s summed by its own walk wave: st (the seed S0, z0 or
 // zero) += totals records 0..s-1, in record order -- the same additions, in
 // the same order, as the prefix scan, so the state is bit-identical (the

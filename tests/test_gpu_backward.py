@@ -79,6 +79,18 @@ def test_sequence_sweep_shapes(N):
     check_backward(q, k, v, g, True, "bf16", label=f"sweep B1H8N{N}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_many_segments_grouped_scan(dtype):
+    # 301 one-chunk segments: the prefix, suffix and total scans take the
+    # grouped form.
+    N = 64 * 300 + 17
+    q, k, v = draw_qkv(1, 2, N, 64, 64, dtype, seed=305)
+    g = draw_grad_output(1, 2, N, 64, dtype, 305)
+    la.set_segments(N)
+    check_backward(q, k, v, g, True, dtype, label="301 segments")
+    check_backward(q, k, v, g, False, dtype, label="301 segments noncausal")
+
+
 def test_mixed_scales():
     gen = torch.Generator().manual_seed(55)
     q = (torch.randn(1, 2, 700, 64, generator=gen) * 3).to(torch.bfloat16)

@@ -53,6 +53,28 @@ def test_sequence_sweep_shapes(N):
     check_forward(q, k, v, True, "bf16", label=f"sweep B1H8N{N}")
 
 
+# 301 one-chunk segments: the prefix and total scans take the grouped form
+# (runs of records per thread group), here also seeded with a carried state.
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_many_segments_grouped_scan(dtype):
+    N = 64 * 300 + 17
+    q, k, v = draw_qkv(1, 2, N, 64, 64, dtype, seed=303)
+    la.set_segments(N)
+    assert la.plan_segments(1, 2, N, q.dtype, True) == 301
+    check_forward(q, k, v, True, dtype, label="301 segments")
+    check_forward(q, k, v, False, dtype, label="301 segments noncausal")
+    g = torch.Generator().manual_seed(304)
+    S0 = torch.rand(2, 64, 64, generator=g).cuda()
+    z0 = (torch.rand(2, 64, generator=g) + 1.0).cuda()
+    o, S1, z1 = la.forward_state(q.cuda(), k.cuda(), v.cuda(), S0=S0, z0=z0)
+    torch.cuda.synchronize()
+    got = o.float().cpu().double().numpy()
+    (ref, S_ref, z_ref), mag = oracle_forward(q, k, v, True, S0=S0.cpu(), z0=z0.cpu(), return_state=True)
+    err, stats = oracle.parity_error(got, ref, mag)
+    note(f"[parity] 301 segments seeded {dtype} err={err:.3e} stats={stats}")
+    assert err <= TOL[dtype]
+
+
 def test_mixed_scales_and_large_magnitudes():
     # Inputs far from N(0, 1): both phi branches, large positive features.
     g = torch.Generator().manual_seed(5)
