@@ -8,9 +8,12 @@ over the long-context workload B=2, H=8, N=131072, C=M=64: the chunk
 kernels, the segment scan and the causal walk.  `value` is whole-job
 tokens/s (B*N sequence positions per second, every head included) with the
 inputs resident in HBM.  The same run also times
+  * the same forward as single cold calls (a 512 MB read between calls
+    evicts the caches), and a plain device copy for the measured ceiling,
   * the recurrent decode step on 256 sequences x 8 heads for 3072 steps
-    (captured in one HIP graph, one kernel per step),
-  * the non-causal forward on B=8, H=8, N=4096,
+    (captured in one HIP graph, one kernel per step), and on 8x the heads,
+  * the causal forward on B=16, H=8, N=3072 and the non-causal forward on
+    B=8, H=8, N=4096, warm and cold,
   * the backward (dQ, dK, dV) of the headline and CIFAR-shaped workloads,
   * forward and forward+backward time and peak memory for N = 2^9..2^16,
   * images/s of greedy generation with a random-weight 12-layer shell
