@@ -177,24 +177,18 @@ __device__ inline f32x4 transpose_tile(const Frag<E> &x, const Frag<E> &ident) {
 }
 
 // ---------------------------------------------------------------------------
-// Global tile I/O.  A 16-row slab of a [rows][64] matrix is read so that lane
-// (n, g) receives row n's columns pi(kt, g, 0..3) for kt = 0..3: two 8-column
-// runs, at columns 8g and 32 + 8g.
+// fp32 row slabs.  A 16-row slab of a [rows][64] matrix is held so that lane
+// (n, g) has row n's columns pi(kt, g, 0..3) for kt = 0..3: two 8-column
+// runs, at columns 8g and 32 + 8g.  The forward kernels fill slabs from a
+// chunk staged in LDS, the fp32 backward straight from global memory.
 // ---------------------------------------------------------------------------
 template <class E> struct Slab;  // raw (unconverted) data of one lane's row piece
 
-template <> struct Slab<__bf16> {
-  u32x4 h[2];  // h[x] = 8 bf16 at columns 32x + 8g
-};
 template <> struct Slab<float> {
   f32x4 h[2][2];  // h[x][y] = 4 floats at columns 32x + 8g + 4y
 };
 
 template <class E> __device__ inline void slab_zero(Slab<E> &s);
-template <> __device__ inline void slab_zero<__bf16>(Slab<__bf16> &s) {
-  s.h[0] = u32x4{0u, 0u, 0u, 0u};
-  s.h[1] = u32x4{0u, 0u, 0u, 0u};
-}
 template <> __device__ inline void slab_zero<float>(Slab<float> &s) {
   for (int x = 0; x < 2; ++x)
     for (int y = 0; y < 2; ++y) s.h[x][y] = zero4();
@@ -202,11 +196,6 @@ template <> __device__ inline void slab_zero<float>(Slab<float> &s) {
 
 // row points at the first element of the lane's row.
 template <class E> __device__ inline void slab_load(Slab<E> &s, const E *row, int g);
-template <> __device__ inline void slab_load<__bf16>(Slab<__bf16> &s, const __bf16 *row, int g) {
-  const u32x4 *p = reinterpret_cast<const u32x4 *>(row);
-  s.h[0] = __builtin_nontemporal_load(p + g);
-  s.h[1] = __builtin_nontemporal_load(p + 4 + g);
-}
 template <> __device__ inline void slab_load<float>(Slab<float> &s, const float *row, int g) {
   const f32x4 *p = reinterpret_cast<const f32x4 *>(row);
   s.h[0][0] = __builtin_nontemporal_load(p + 2 * g);
@@ -215,28 +204,9 @@ template <> __device__ inline void slab_load<float>(Slab<float> &s, const float 
   s.h[1][1] = __builtin_nontemporal_load(p + 8 + 2 * g + 1);
 }
 
-// Slab -> 4 operand fragments (kt = 0..3), optionally through phi, optionally
-// forced to zero (rows past the end of the sequence).
+// Slab -> 4 operand fragments (kt = 0..3), optionally through phi.
 template <class E> __device__ inline void slab_to_frags(const Slab<E> &s, Frag<E> f[4], bool apply_phi);
 
-template <>
-__device__ inline void slab_to_frags<__bf16>(const Slab<__bf16> &s, Frag<__bf16> f[4], bool apply_phi) {
-  for (int x = 0; x < 2; ++x) {
-    const uint32_t w[4] = {s.h[x][0], s.h[x][1], s.h[x][2], s.h[x][3]};
-    uint32_t o[4];
-    for (int i = 0; i < 4; ++i) {
-      if (apply_phi) {
-        o[i] = pack_bf16(phi(bf16_lo(w[i])), phi(bf16_hi(w[i])));
-      } else {
-        o[i] = w[i];
-      }
-    }
-    f[2 * x].w[0] = o[0];
-    f[2 * x].w[1] = o[1];
-    f[2 * x + 1].w[0] = o[2];
-    f[2 * x + 1].w[1] = o[3];
-  }
-}
 template <>
 __device__ inline void slab_to_frags<float>(const Slab<float> &s, Frag<float> f[4], bool apply_phi) {
   for (int x = 0; x < 2; ++x)
@@ -251,12 +221,6 @@ __device__ inline void slab_to_frags<float>(const Slab<float> &s, Frag<float> f[
 // Store 8 output values of one row at columns 32x + 8g (two transposed output
 // tiles 2x and 2x+1, register r = column 32x + 8g + 4y + r).
 template <class E> __device__ inline void store_row8(E *row, int g, int x, f32x4 lo, f32x4 hi);
-template <>
-__device__ inline void store_row8<__bf16>(__bf16 *row, int g, int x, f32x4 lo, f32x4 hi) {
-  const u32x4 v = {pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(hi[0], hi[1]),
-                   pack_bf16(hi[2], hi[3])};
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(row) + 4 * x + g);
-}
 template <>
 __device__ inline void store_row8<float>(float *row, int g, int x, f32x4 lo, f32x4 hi) {
   f32x4 *p = reinterpret_cast<f32x4 *>(row) + 8 * x + 2 * g;

@@ -281,27 +281,51 @@ __device__ inline void stream_lds(u32x4 *slot, const __bf16 *const src[kTensors]
 }
 
 // ---------------------------------------------------------------------------
-// fp32 path: register slabs straight from global memory, one chunk at a time
-// (an fp32 chunk is twice the size; latency is hidden by the other waves).
+// fp32 path.
 // ---------------------------------------------------------------------------
-template <class E> struct Chunk {
-  Slab<E> t[3][4];  // [tensor][row tile]
-};
-
-template <class E, int kTensors>
-__device__ inline void chunk_load(Chunk<E> &d, const E *const src[kTensors], long long t0, int rows, int n16, int g) {
+// fp32 chunks staged in LDS.  A row is 64 floats, sixteen 16-byte pieces;
+// piece p of row r of a tensor's region sits at 16-byte unit
+// 16 r + (p ^ (r & 15)), so that the sixteen rows a row-layout read touches
+// at once fall on different banks.  One load instruction fetches four whole
+// rows: lane l loads row 4i + (l >> 4), piece (l & 15) ^ (row & 15), and its
+// bytes land at unit 64 i + l.
+template <int kTensors, int NT>
+__device__ inline void stage_issue_f32(u32x4 *slot, const float *const src[kTensors], long long t0, int rows,
+                                       int lane) {
+  const int sub = lane >> 4;
 #pragma unroll
-  for (int tsr = 0; tsr < kTensors; ++tsr)
+  for (int tsr = 0; tsr < kTensors; ++tsr) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int row = 16 * it + n16;
-      if (row < rows) {
-        slab_load<E>(d.t[tsr][it], src[tsr] + (t0 + row) * kD, g);
-      } else {
-        slab_zero<E>(d.t[tsr][it]);
-      }
+    for (int i = 0; i < 4 * NT; ++i) {
+      const int row = 4 * i + sub;
+      const int piece = (lane & 15) ^ (row & 15);
+      if (row < rows)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4 *>(src[tsr] + (t0 + row) * kD) + piece,
+                                         (lds_void *)(slot + (tsr * 16 * NT + 4 * i) * 16), 16, 0, kLoadDefault);
     }
+  }
 }
+
+// The slab of row tile it of tensor tsr (rows past `rows` read as zero: the
+// slot still holds an earlier chunk there, or nothing yet).
+template <int NT>
+__device__ inline void slab_from_lds_f32(Slab<float> &s, const u32x4 *slot, int tsr, int it, int rows, int n16,
+                                         int g) {
+  const int R = 16 * it + n16;
+  if (R >= rows) {
+    slab_zero<float>(s);
+    return;
+  }
+  const u32x4 *row = slot + (tsr * 16 * NT + R) * 16;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) s.h[x][y] = __builtin_bit_cast(f32x4, row[(8 * x + 2 * g + y) ^ (R & 15)]);
+}
+
+// Row tiles per chunk of the fp32 walk: 32-token chunks, so that Q, K and V
+// of one chunk (24 KB) stage in LDS like the bf16 walk's 64-token chunk.
+constexpr int kWalkTilesF32 = 2;
 
 // Token layout from row layout by an identity product (exact).
 template <class E, int NT = 4>
@@ -459,20 +483,31 @@ __global__ __launch_bounds__(64, 1) void seg_totals_kernel(FwdParams p, int tota
       state_update<E>(st, kt, vt);
     });
   } else {
+    // fp32: K and V of a 64-token chunk (32 KB) staged in LDS, the next
+    // chunk's loads in flight while this one is computed.
     const Frag<E> ident = frag_identity<E>(n16, g);
-    const E *src[2] = {Kh, Vh};
+    constexpr int NT = 4;
+    __shared__ u32x4 slot[2 * 16 * NT * 16];
+    const float *src[2] = {Kh, Vh};
+    if (t_begin < t_end) stage_issue_f32<2, NT>(slot, src, t_begin, chunk_rows(t_begin, t_end), lane);
     for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
       const int rows = chunk_rows(t0, t_end);
-      Chunk<E> d;
-      chunk_load<E, 2>(d, src, t0, rows, n16, g);
+      wait_vmcnt<0>();  // no stores: everything outstanding is this chunk's loads
+      Slab<float> d[2][NT];
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt)
+#pragma unroll
+        for (int tsr = 0; tsr < 2; ++tsr) slab_from_lds_f32<NT>(d[tsr][jt], slot, tsr, jt, rows, n16, g);
+      wait_lgkmcnt0();
+      if (t0 + kChunk < t_end) stage_issue_f32<2, NT>(slot, src, t0 + kChunk, chunk_rows(t0 + kChunk, t_end), lane);
       Frag<E> kf[4][4], vf[4][4], kt[4][4], vt[4][4];
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) {
-        slab_to_frags<E>(d.t[0][jt], kf[jt], true);
+        slab_to_frags<E>(d[0][jt], kf[jt], true);
         if (16 * jt + n16 >= rows)
 #pragma unroll
           for (int c = 0; c < 4; ++c) kf[jt][c] = frag_zero<E>();
-        slab_to_frags<E>(d.t[1][jt], vf[jt], false);
+        slab_to_frags<E>(d[1][jt], vf[jt], false);
       }
       row_to_tok<E>(kf, kt, ident);
       row_to_tok<E>(vf, vt, ident);
@@ -839,25 +874,44 @@ __device__ inline void causal_walk(const FwdParams &p) {
       }
     }
   } else {
+    // fp32: 32-token chunks staged in LDS; the next chunk's loads are in
+    // flight while this one is computed.
+    constexpr int NT = kWalkTilesF32;
+    constexpr int kT = 16 * NT;
+    constexpr int kStores = 4 * NT;  // output stores of a full chunk
+    __shared__ u32x4 slot[3 * 16 * NT * 16];
+    const float *src[3] = {Qh, Kh, Vh};
+    if (t_begin < t_end) stage_issue_f32<3, NT>(slot, src, t_begin, (int)min<long long>(kT, t_end - t_begin), lane);
     init_state();
-    const E *src[3] = {Qh, Kh, Vh};
-    for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
-      const int rows = chunk_rows(t0, t_end);
-      Chunk<E> d;
-      chunk_load<E, 3>(d, src, t0, rows, n16, g);
-      Frag<E> qf[4][4], kf[4][4], vf[4][4], kt[4][4], vt[4][4];
+    for (long long t0 = t_begin; t0 < t_end; t0 += kT) {
+      const int rows = (int)min<long long>(kT, t_end - t0);
+      // Outstanding: this chunk's loads, then the previous (full) chunk's
+      // stores; they retire in order.
+      if (t0 == t_begin) {
+        wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<kStores>();
+      }
+      Slab<float> d[3][NT];
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        slab_to_frags<E>(d.t[0][it], qf[it], true);
-        slab_to_frags<E>(d.t[1][it], kf[it], true);
+      for (int it = 0; it < NT; ++it)
+#pragma unroll
+        for (int tsr = 0; tsr < 3; ++tsr) slab_from_lds_f32<NT>(d[tsr][it], slot, tsr, it, rows, n16, g);
+      wait_lgkmcnt0();  // the slot is refilled only after every lane's read of it returned
+      if (t0 + kT < t_end) stage_issue_f32<3, NT>(slot, src, t0 + kT, (int)min<long long>(kT, t_end - t0 - kT), lane);
+      Frag<E> qf[NT][4], kf[NT][4], vf[NT][4], kt[NT][4], vt[NT][4];
+#pragma unroll
+      for (int it = 0; it < NT; ++it) {
+        slab_to_frags<E>(d[0][it], qf[it], true);
+        slab_to_frags<E>(d[1][it], kf[it], true);
         if (16 * it + n16 >= rows)
 #pragma unroll
           for (int c = 0; c < 4; ++c) kf[it][c] = frag_zero<E>();
-        slab_to_frags<E>(d.t[2][it], vf[it], false);
+        slab_to_frags<E>(d[2][it], vf[it], false);
       }
-      row_to_tok<E>(kf, kt, ident);
-      row_to_tok<E>(vf, vt, ident);
-      causal_chunk<E, 4, false>(st, qf, kf, kt, vt, rows, Oh, t0, n16, g);
+      row_to_tok<E, NT>(kf, kt, ident);
+      row_to_tok<E, NT>(vf, vt, ident);
+      causal_chunk<E, NT, false>(st, qf, kf, kt, vt, rows, Oh, t0, n16, g);
     }
   }
   if (p.S_out != nullptr && s == p.segments - 1)
@@ -923,15 +977,29 @@ __global__ __launch_bounds__(64, 1) void noncausal_read_kernel(FwdParams p, int 
       }
     }
   } else {
-    const E *src[1] = {Qh};
+    // fp32: Q of a 64-token chunk (16 KB) staged in LDS, the next chunk's
+    // loads in flight while this one is computed.
+    constexpr int NT = 4;
+    constexpr int kStores = 4 * NT;  // output stores of a full chunk
+    __shared__ u32x4 slot[16 * NT * 16];
+    const float *src[1] = {Qh};
+    if (t_begin < t_end) stage_issue_f32<1, NT>(slot, src, t_begin, chunk_rows(t_begin, t_end), lane);
     for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
       const int rows = chunk_rows(t0, t_end);
-      Chunk<E> d;
-      chunk_load<E, 1>(d, src, t0, rows, n16, g);
+      if (t0 == t_begin) {  // see stream_lds
+        wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<kStores>();
+      }
+      Slab<float> d[NT];
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
+      for (int it = 0; it < NT; ++it) slab_from_lds_f32<NT>(d[it], slot, 0, it, rows, n16, g);
+      wait_lgkmcnt0();
+      if (t0 + kChunk < t_end) stage_issue_f32<1, NT>(slot, src, t0 + kChunk, chunk_rows(t0 + kChunk, t_end), lane);
+#pragma unroll
+      for (int it = 0; it < NT; ++it) {
         Frag<E> qf[4];
-        slab_to_frags<E>(d.t[0][it], qf, true);
+        slab_to_frags<E>(d[it], qf, true);
         f32x4 nt[4] = {zero4(), zero4(), zero4(), zero4()};
         f32x4 dt = zero4();
         state_read<E>(so, qf, nt, dt);
