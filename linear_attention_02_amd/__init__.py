@@ -127,6 +127,7 @@ def _dt(t) -> int:
 
 
 def _check_cuda(*ts):
+    device = None
     for t in ts:
         if t is None:
             continue
@@ -134,6 +135,10 @@ def _check_cuda(*ts):
             raise LinattnError(8, "tensors must be on a GPU device (no CPU fallback exists)")
         if not t.is_contiguous():
             raise LinattnError(8, "tensors must be contiguous")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise LinattnError(8, f"tensors must be on one device (found {device} and {t.device})")
 
 
 def _stream(stream, device) -> int:
@@ -169,6 +174,8 @@ def _alloc_ws(nbytes: int, device, workspace):
     if nbytes == 0:
         return None
     if workspace is not None:
+        if workspace.device != device or not workspace.is_contiguous():
+            raise LinattnError(8, "workspace must be a contiguous tensor on the inputs' device")
         if workspace.numel() * workspace.element_size() < nbytes:
             raise LinattnError(6, f"workspace needs {nbytes} bytes")
         return workspace
@@ -328,6 +335,8 @@ def decode_step_strided(S, z, q, k, v, out=None, stream=None):
             raise LinattnError(8, "tensors must be on a GPU device (no CPU fallback exists)")
         if t.dim() != 2 or t.stride(1) != 1:
             raise LinattnError(2, "q, k, v must be 2-D with unit column stride")
+    if any(t.device != S.device for t in (q, k, v)):
+        raise LinattnError(8, "q, k, v and the state must be on one device")
     stride = q.stride(0)
     if k.stride(0) != stride or v.stride(0) != stride:
         raise LinattnError(2, "q, k and v must share one row stride")
