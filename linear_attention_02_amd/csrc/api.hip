@@ -160,7 +160,11 @@ linattn_status run_forward(const FwdParams &base, const Plan &plan, int causal, 
                            p, plan.segments - 1);
       }
       if (launch_error("seg_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
-      if (sum_in_walk(plan.segments)) {
+      // Summing in the walk, every wave reads S0, z0 at its start while the last
+      // segment's wave writes S_out, z_out at its end: an in-place call
+      // (S_out == S0) takes the scan, which reads S0, z0 in a launch of its own.
+      const bool in_place = p.S0 != nullptr && (p.S_out == p.S0 || p.z_out == p.z0);
+      if (sum_in_walk(plan.segments) && !in_place) {
         p.init = kInitTotals;
       } else {
         {

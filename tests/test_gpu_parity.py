@@ -165,7 +165,8 @@ def test_forward_state_in_place_and_empty():
     assert torch.equal(S_out, S_keep) and torch.equal(z_out, z_keep)
     q, k, v = [t.cuda() for t in draw_qkv(1, 2, 200, 64, 64, "f32", seed=2)]
     ref_o, ref_S, ref_z = la.forward_state(q, k, v, S0=S_keep, z0=z_keep)
-    o, S_out, z_out = la.forward_state(q, k, v, S0=S, z0=z, S_out=S, z_out=z)  # in place
+    # In place (4 segments: the prefix scan reads S0, z0 before the walk writes them).
+    o, S_out, z_out = la.forward_state(q, k, v, S0=S, z0=z, S_out=S, z_out=z)
     torch.cuda.synchronize()
     assert torch.equal(o, ref_o) and torch.equal(S, ref_S) and torch.equal(z, ref_z)
 
