@@ -3,7 +3,8 @@
 //
 // Every kernel in this library is built from 16x16 MFMA tiles.  One wave64 is
 // one independent worker; data moves between the operand and accumulator
-// layouts entirely in registers (no LDS), using two facts about CDNA MFMAs:
+// layouts in registers (the LDS only stages each wave's own input chunks),
+// using two facts about CDNA MFMAs:
 //
 //   * accumulator ("C") layout of a 16x16 tile: lane l holds D[4g+r][n] for
 //     r = 0..3, where n = l & 15 and g = l >> 4;

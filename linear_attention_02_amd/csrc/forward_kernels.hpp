@@ -919,7 +919,7 @@ __device__ inline void causal_walk(const FwdParams &p) {
 }
 
 // One wave per SIMD: the walk keeps the state, one chunk's fragments and the
-// products' accumulators in registers (about 400 of the 512).
+// products' accumulators in registers (about 480 of the 512).
 __global__ __launch_bounds__(64, 1) void causal_walk_kernel_bf16(FwdParams p) { causal_walk<__bf16>(p); }
 __global__ __launch_bounds__(64, 1) void causal_walk_kernel_f32(FwdParams p) { causal_walk<float>(p); }
 template <class E> struct WalkKernel;

@@ -23,7 +23,7 @@ constexpr size_t kStateBytes = (4096 + 64) * sizeof(float);
 constexpr long long kMinSegmentChunks = 4;
 constexpr long long kMaxShortSegments = 64;
 // Workers (waves) aimed for per compute unit: one per SIMD (the walk kernel
-// holds about 400 registers per lane).
+// holds about 480 registers per lane).
 constexpr long long kWavesPerCU = 4;
 
 Check fail(linattn_status s, const std::string &msg) {
