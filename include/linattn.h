@@ -12,8 +12,24 @@
  *   o_i = phi(q_i)^T S_i / phi(q_i)^T z_i
  *
  * with J(i) = {0..i} (causal, inclusive) or {0..N-1} (non-causal).  There is
- * no epsilon in the denominator: phi > 0, so every denominator is positive
- * for finite inputs.
+ * no epsilon in the denominator.  In exact arithmetic phi > 0, so every
+ * denominator is positive ("Why Replace Attention?", §5.4); in fp32 it can
+ * underflow or overflow, the failure the "Transformers Are RNNs: Linear
+ * Attention" knowledge note warns of under "Where It Breaks".
+ *
+ * Range.  o_i does not change when phi(q_i) is multiplied by a positive
+ * constant, so the kernels scale each query row's phi(q_i) by an exact power
+ * of two whenever its largest feature lies outside [-8, 65535] (the largest
+ * scaled value then lies in [1, 2)); rows inside that interval are not
+ * scaled, which changes no rounding.  Any finite query row is therefore
+ * supported.  The supported range of keys and values is:
+ *   every K feature >= -60, and N * (1 + max K) * max(1, max |V|) <= 2^100;
+ * there outputs meet the library's accuracy (max |o - o_exact| / o_mag
+ * <= 1e-4 for fp32 inputs, <= 2e-2 for bf16 inputs, with o_mag the same
+ * weighted mean of |v|).  Below -60, accuracy degrades gradually.  When
+ * every key feature that query i sees is below -104, e^x is 0 in fp32,
+ * the denominator is exactly 0 and o_i is NaN (a decode step likewise,
+ * while the state holds only such keys).  Inputs must be finite.
  *
  * Conventions shared by every entry point:
  *   - Pointers are device pointers (hipMalloc / PyTorch CUDA tensors) unless a
@@ -138,6 +154,9 @@ size_t linattn_backward_workspace_bytes(int B, int H, int N, int C, int M, linat
  *   R_j = sum_{i: j in J(i)} phi(q_i) a_i^T,  r_j = sum_{i: j in J(i)} b_i phi(q_i)
  *   dq = dphi(q) * phi'(q),  phi'(x) = 1 for x > 0, e^x otherwise.
  * o_i is recomputed in fp32 (the forward's output is not an argument).
+ * Range: the backward does not scale query rows, so on top of the forward's
+ * range it needs every query row's largest feature in [-60, 2^30]; outside
+ * it gradients may be NaN or inaccurate where the forward is not.
  *
  * Q, K, V, dO: [B,H,N,64] in `dt`; dQ, dK, dV: [B,H,N,64] in `dt`, written.
  * causal as in linattn_forward.  Accumulation is fp32; bf16 outputs are

@@ -182,6 +182,28 @@ def _alloc_ws(nbytes: int, device, workspace):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
+def _check_like(name: str, t, ref):
+    """A caller-supplied output must match ``ref`` in shape and dtype: the
+    library sizes every access from the input's shape and element type."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(ref.shape):
+        raise LinattnError(2, f"{name} must have shape {tuple(ref.shape)}, got {tuple(t.shape)}")
+    if t.dtype != ref.dtype:
+        raise LinattnError(3, f"{name} must be {ref.dtype}, got {t.dtype}")
+
+
+def _check_state(name: str, t, numel: int):
+    """A state buffer is float32 with exactly ``numel`` elements."""
+    if t is None:
+        return
+    torch = _torch()
+    if t.dtype != torch.float32:
+        raise LinattnError(3, f"{name} must be float32, got {t.dtype}")
+    if t.numel() != numel:
+        raise LinattnError(2, f"{name} must have {numel} elements, got {t.numel()}")
+
+
 def _shape(q, k, v):
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise LinattnError(2, f"expected q, k [B,H,N,C] and v [B,H,N,M]; got {tuple(q.shape)}, "
@@ -195,9 +217,10 @@ def _shape(q, k, v):
 def forward(q, k, v, causal: bool = True, out=None, workspace=None, stream=None):
     """Chunked parallel forward; returns o [B,H,N,M] in the input dtype."""
     torch = _torch()
-    _check_cuda(q, k, v, out)
     B, H, N, C, M = _shape(q, k, v)
     dt = _dt(q)
+    _check_like("out", out, v)
+    _check_cuda(q, k, v, out)
     if out is None:
         out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
     nbytes = int(lib().linattn_forward_workspace_bytes(B, H, N, C, M, dt, int(bool(causal))))
@@ -214,17 +237,18 @@ def forward_state(q, k, v, S0=None, z0=None, out=None, S_out=None, z_out=None, w
     S0/S_out: [B*H, C, M] float32 (or [B, H, C, M]); z0/z_out: [B*H, C] float32.
     """
     torch = _torch()
-    _check_cuda(q, k, v, S0, z0, out, S_out, z_out)
     B, H, N, C, M = _shape(q, k, v)
     dt = _dt(q)
+    _check_like("out", out, v)
+    for name, t, n in (("S0", S0, B * H * C * M), ("z0", z0, B * H * C), ("S_out", S_out, B * H * C * M),
+                       ("z_out", z_out, B * H * C)):
+        _check_state(name, t, n)
+    _check_cuda(q, k, v, S0, z0, out, S_out, z_out)
     if out is None:
         out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
     if return_state and S_out is None:
         S_out = torch.empty((B * H, C, M), dtype=torch.float32, device=q.device)
         z_out = torch.empty((B * H, C), dtype=torch.float32, device=q.device)
-    for t in (S0, z0, S_out, z_out):
-        if t is not None and t.dtype != torch.float32:
-            raise LinattnError(3, "states are float32")
     nbytes = int(lib().linattn_forward_state_workspace_bytes(B, H, N, C, M, dt))
     ws = _alloc_ws(nbytes, q.device, workspace)
     _call(q.device, lib().linattn_forward_state, _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, C, M, dt, _ptr(S0),
@@ -246,11 +270,14 @@ def backward(q, k, v, grad_out, causal: bool = True, dq=None, dk=None, dv=None, 
     records it holds are reused instead of recomputed.
     """
     torch = _torch()
-    _check_cuda(q, k, v, grad_out, dq, dk, dv)
     B, H, N, C, M = _shape(q, k, v)
     if grad_out.shape != v.shape or grad_out.dtype != v.dtype:
         raise LinattnError(2, "grad_out must match v in shape and dtype")
     dt = _dt(q)
+    _check_like("dq", dq, q)
+    _check_like("dk", dk, k)
+    _check_like("dv", dv, v)
+    _check_cuda(q, k, v, grad_out, dq, dk, dv)
     dq = torch.empty(q.shape, dtype=q.dtype, device=q.device) if dq is None else dq
     dk = torch.empty(k.shape, dtype=k.dtype, device=k.device) if dk is None else dk
     dv = torch.empty(v.shape, dtype=v.dtype, device=v.device) if dv is None else dv
@@ -270,17 +297,19 @@ def decode_step(S, z, q, k, v, out=None, stream=None):
     q, k: [BH, C]; v: [BH, M] in float32 or bfloat16.  Returns o [BH, M] float32.
     """
     torch = _torch()
-    _check_cuda(S, z, q, k, v, out)
-    if S.dtype != torch.float32 or z.dtype != torch.float32:
-        raise LinattnError(3, "S and z are float32")
-    BH = q.shape[0]
-    C = q.shape[-1]
-    M = v.shape[-1]
-    if k.shape != q.shape or v.shape[0] != BH or S.numel() != BH * C * M or z.numel() != BH * C:
+    if q.dim() != 2 or v.dim() != 2:
+        raise LinattnError(2, "q, k must be [BH, C] and v [BH, M]")
+    BH, C = q.shape
+    M = v.shape[1]
+    if k.shape != q.shape or v.shape[0] != BH:
         raise LinattnError(2, "decode_step shape mismatch")
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise LinattnError(3, "q, k and v must share one dtype")
     dt = _dt(q)
+    _check_state("S", S, BH * C * M)
+    _check_state("z", z, BH * C)
+    _check_state("out", out, BH * M)
+    _check_cuda(S, z, q, k, v, out)
     if out is None:
         out = torch.empty((BH, M), dtype=torch.float32, device=q.device)
     _call(q.device, lib().linattn_decode_step, _ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), BH, C, M, dt,
@@ -329,25 +358,28 @@ def decode_step_strided(S, z, q, k, v, out=None, stream=None):
     """decode_step for q, k, v given as [BH, 64] views that share one row
     stride (e.g. column slices of a [BH, 3 * 64] projection output)."""
     torch = _torch()
-    _check_cuda(S, z, out)
     for t in (q, k, v):
-        if not t.is_cuda:
-            raise LinattnError(8, "tensors must be on a GPU device (no CPU fallback exists)")
         if t.dim() != 2 or t.stride(1) != 1:
             raise LinattnError(2, "q, k, v must be 2-D with unit column stride")
-    if any(t.device != S.device for t in (q, k, v)):
-        raise LinattnError(8, "q, k, v and the state must be on one device")
     stride = q.stride(0)
     if k.stride(0) != stride or v.stride(0) != stride:
         raise LinattnError(2, "q, k and v must share one row stride")
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise LinattnError(3, "q, k and v must share one dtype")
-    if S.dtype != torch.float32 or z.dtype != torch.float32:
-        raise LinattnError(3, "S and z are float32")
+    _dt(q)
     BH, C = q.shape
     M = v.shape[1]
-    if k.shape != q.shape or v.shape[0] != BH or S.numel() != BH * C * M or z.numel() != BH * C:
+    if k.shape != q.shape or v.shape[0] != BH:
         raise LinattnError(2, "decode_step_strided shape mismatch")
+    _check_state("S", S, BH * C * M)
+    _check_state("z", z, BH * C)
+    _check_state("out", out, BH * M)
+    _check_cuda(S, z, out)
+    for t in (q, k, v):
+        if not t.is_cuda:
+            raise LinattnError(8, "tensors must be on a GPU device (no CPU fallback exists)")
+    if any(t.device != S.device for t in (q, k, v)):
+        raise LinattnError(8, "q, k, v and the state must be on one device")
     if out is None:
         out = torch.empty((BH, M), dtype=torch.float32, device=q.device)
     _call(q.device, lib().linattn_decode_step_strided, _ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), BH,

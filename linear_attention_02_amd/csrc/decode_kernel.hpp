@@ -25,6 +25,41 @@ template <> __device__ inline float load_elem<__bf16>(const __bf16 *p, int i) {
   return __uint_as_float((uint32_t)(reinterpret_cast<const uint16_t *>(p)[i]) << 16);
 }
 
+// Elements 16c .. 16c + 15 of a 64-element row as fp32, in 16-byte loads
+// (four for fp32, two for bf16).  Rows are 16-byte aligned.
+template <class E> __device__ inline void load16(const E *row, int c, float out[16]);
+template <> __device__ inline void load16<float>(const float *row, int c, float out[16]) {
+  const f32x4 *p = reinterpret_cast<const f32x4 *>(row) + 4 * c;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 x = p[i];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[4 * i + r] = x[r];
+  }
+}
+template <> __device__ inline void load16<__bf16>(const __bf16 *row, int c, float out[16]) {
+  const u32x4 *p = reinterpret_cast<const u32x4 *>(row) + 2 * c;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const u32x4 x = p[i];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      out[8 * i + 2 * r] = bf16_lo(x[r]);
+      out[8 * i + 2 * r + 1] = bf16_hi(x[r]);
+    }
+  }
+}
+
+// Elements 4c .. 4c + 3 (one 16-byte fp32 load, one 8-byte bf16 load).
+template <class E> __device__ inline f32x4 load4(const E *row, int c);
+template <> __device__ inline f32x4 load4<float>(const float *row, int c) {
+  return reinterpret_cast<const f32x4 *>(row)[c];
+}
+template <> __device__ inline f32x4 load4<__bf16>(const __bf16 *row, int c) {
+  const u32x2 x = reinterpret_cast<const u32x2 *>(row)[c];
+  return f32x4{bf16_lo(x[0]), bf16_hi(x[0]), bf16_lo(x[1]), bf16_hi(x[1])};
+}
+
 template <class E>
 __global__ __launch_bounds__(256) void decode_step_kernel(float *__restrict__ S, float *__restrict__ z,
                                                           const E *__restrict__ q, const E *__restrict__ k,
@@ -40,15 +75,27 @@ __global__ __launch_bounds__(256) void decode_step_kernel(float *__restrict__ S,
   const E *vh = v + (long long)h * stride;
   float4 *Sh = reinterpret_cast<float4 *>(S + (long long)h * kD * kD);
 
-  // phi(k), phi(q) for this lane's 16 rows; v for its 4 columns.
-  float pk[16], pq[16];
+  // q, k for this lane's 16 rows; v for its 4 columns.
+  float qr[16], pk[16], pq[16];
+  load16<E>(qh, cq, qr);
+  load16<E>(kh, cq, pk);
+  const f32x4 vv = load4<E>(vh, m4);
+  const float v0 = vv[0], v1 = vv[1], v2 = vv[2], v3 = vv[3];
+  // phi(q) scaled by the power of two phi_row_scale picks from the largest
+  // of the 64 features (the same for the whole wave; o does not change).
+  float qmax = qr[0];
+#pragma unroll
+  for (int rr = 1; rr < 16; ++rr) qmax = fmaxf(qmax, qr[rr]);
+  qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
+  qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
+  float eneg;
+  int epos;
+  phi_row_scale(qmax, eneg, epos);
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
-    pk[rr] = phi(load_elem<E>(kh, 16 * cq + rr));
-    pq[rr] = phi(load_elem<E>(qh, 16 * cq + rr));
+    pk[rr] = phi(pk[rr]);
+    pq[rr] = phi_row_scaled(qr[rr], eneg, epos);
   }
-  const float v0 = load_elem<E>(vh, 4 * m4 + 0), v1 = load_elem<E>(vh, 4 * m4 + 1);
-  const float v2 = load_elem<E>(vh, 4 * m4 + 2), v3 = load_elem<E>(vh, 4 * m4 + 3);
 
   // Rank-1 update S += phi(k) v^T, then the partial read phi(q)^T S.
   float4 s[16];
@@ -73,7 +120,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(float *__restrict__ S,
   float *zh = z + (long long)h * kD;
   const float zl = zh[lane] + phi(load_elem<E>(kh, lane));
   zh[lane] = zl;
-  float den = phi(load_elem<E>(qh, lane)) * zl;
+  float den = phi_row_scaled(load_elem<E>(qh, lane), eneg, epos) * zl;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
 

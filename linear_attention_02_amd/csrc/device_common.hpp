@@ -57,6 +57,44 @@ __device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // ---------------------------------------------------------------------------
 __device__ inline float phi(float x) { return __builtin_amdgcn_fmed3f(x + 1.f, __expf(x), 1.f); }
 
+// ---------------------------------------------------------------------------
+// The scale of one query row's phi(q).
+//
+// o_i is a ratio of two sums that are both linear in phi(q_i), so o_i does not
+// change when phi(q_i) is multiplied by any positive constant ("Why Replace
+// Attention?", §5.4: the weights are normalised per query).  A power of two
+// changes no rounding, so it changes nothing at all unless the unscaled row
+// would leave fp32's range: a row whose features are all far below zero has
+// e^x underflow (at x < -87 in fp32), and a row with features near 1e19 or
+// beyond overflows its products with phi(K).  Rows whose largest feature m
+// lies in [kPhiQLow, kPhiQHigh] keep phi unchanged; the others are scaled so
+// that their largest phi lies in [1, 2):
+//   m > kPhiQHigh:  phi(x) * 2^-e with e = floor(log2(m + 1));
+//   m < kPhiQLow:   e^x * 2^-e = 2^(x log2(e) - e) with e = floor(m log2(e)),
+//                   evaluated as one exp2 so that nothing underflows first.
+// ---------------------------------------------------------------------------
+constexpr float kPhiQLow = -8.f;
+constexpr float kPhiQHigh = 65535.f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// phi(x) * 2^-(epos) when eneg == 0, else 2^(x log2(e) - eneg) (eneg < 0 is an
+// integer; then every feature of the row is below kPhiQLow).
+__device__ inline float phi_row_scaled(float x, float eneg, int epos) {
+  const float p = eneg != 0.f ? __builtin_amdgcn_exp2f(x * kLog2e - eneg) : phi(x);
+  return __builtin_amdgcn_ldexpf(p, -epos);
+}
+
+// The row scale (eneg, epos) from the row's largest raw feature m.
+__device__ inline void phi_row_scale(float m, float &eneg, int &epos) {
+  eneg = 0.f;
+  epos = 0;
+  if (m > kPhiQHigh) {
+    epos = __builtin_amdgcn_frexp_expf(m + 1.f) - 1;  // m + 1 = f 2^(epos + 1), f in [0.5, 1)
+  } else if (m < kPhiQLow) {
+    eneg = floorf(m * kLog2e);
+  }
+}
+
 // bf16 <-> fp32.  Widening is exact; narrowing is the hardware's
 // round-to-nearest-even conversion of two values at once
 // (v_cvt_pk_bf16_f32).

@@ -163,6 +163,48 @@ template <> __device__ inline void phi_frag<float>(Frag<float> &f) {
 }
 
 // ---------------------------------------------------------------------------
+// phi(Q) of one row tile, each query row scaled as phi_row_scale decides
+// (device_common.hpp).  Lane (n, g) holds 16 of row n's features, so a lane's
+// own maximum decides whether the row can need a scale; only then (rarely:
+// never for inputs of moderate size) does the wave form each row's maximum
+// across its four lanes.  Rows that need no scale get exactly phi.
+// ---------------------------------------------------------------------------
+__device__ inline float raw_elem(const Frag<__bf16> &f, int r) {
+  const uint32_t w = f.w[r >> 1];
+  return (r & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+__device__ inline float raw_elem(const Frag<float> &f, int r) { return f.v[r]; }
+
+template <class E> __device__ inline void phi_q_tile(Frag<E> f[4]) {
+  float m = raw_elem(f[0], 0);
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m = fmaxf(m, raw_elem(f[c], r));
+  if (!__any(m > kPhiQHigh || m < kPhiQLow)) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) phi_frag<E>(f[c]);
+    return;
+  }
+  // Row maximum over the lanes n, n + 16, n + 32, n + 48.
+  m = fmaxf(m, __shfl_xor(m, 16, 64));
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  float eneg;
+  int epos;
+  phi_row_scale(m, eneg, epos);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if constexpr (std::is_same<E, __bf16>::value) {
+      f[c].w[0] = pack_bf16(phi_row_scaled(raw_elem(f[c], 0), eneg, epos), phi_row_scaled(raw_elem(f[c], 1), eneg, epos));
+      f[c].w[1] = pack_bf16(phi_row_scaled(raw_elem(f[c], 2), eneg, epos), phi_row_scaled(raw_elem(f[c], 3), eneg, epos));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) f[c].v[r] = phi_row_scaled(f[c].v[r], eneg, epos);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // bf16 path: chunks staged in LDS.  The next chunk is fetched with
 // global_load_lds_dwordx4 (HBM -> LDS without passing through VGPRs) into a
 // wave-private slot while the current chunk is computed.  Each load
@@ -792,12 +834,11 @@ __device__ inline void causal_chunk_lds(State &st, u32x4 *slot, const __bf16 *co
   wait_lgkmcnt0();  // the slot is refilled only after every lane's read of it returned
   if (t0 + kT < t_end) stage_issue<3, NT>(slot, src, t0 + kT, (int)min<long long>(kT, t_end - t0 - kT), n16, g);
 #pragma unroll
-  for (int it = 0; it < NT; ++it)
+  for (int it = 0; it < NT; ++it) {
+    phi_q_tile<E>(qf[it]);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      phi_frag<E>(qf[it][c]);
-      phi_frag<E>(kf[it][c]);
-    }
+    for (int c = 0; c < 4; ++c) phi_frag<E>(kf[it][c]);
+  }
   if (!kFull) {
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) {
@@ -902,7 +943,8 @@ __device__ inline void causal_walk(const FwdParams &p) {
       Frag<E> qf[NT][4], kf[NT][4], vf[NT][4], kt[NT][4], vt[NT][4];
 #pragma unroll
       for (int it = 0; it < NT; ++it) {
-        slab_to_frags<E>(d[0][it], qf[it], true);
+        slab_to_frags<E>(d[0][it], qf[it], false);
+        phi_q_tile<E>(qf[it]);
         slab_to_frags<E>(d[1][it], kf[it], true);
         if (16 * it + n16 >= rows)
 #pragma unroll
@@ -968,8 +1010,7 @@ __global__ __launch_bounds__(64, 1) void noncausal_read_kernel(FwdParams p, int 
       if (t0 + kChunk < t_end) stage_issue<1>(slot, src, t0 + kChunk, chunk_rows(t0 + kChunk, t_end), n16, g);
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) phi_frag<E>(qf[it][c]);
+        phi_q_tile<E>(qf[it]);
         f32x4 nt[4] = {zero4(), zero4(), zero4(), zero4()};
         f32x4 dt = zero4();
         state_read<E>(so, qf[it], nt, dt);
@@ -999,7 +1040,8 @@ __global__ __launch_bounds__(64, 1) void noncausal_read_kernel(FwdParams p, int 
 #pragma unroll
       for (int it = 0; it < NT; ++it) {
         Frag<E> qf[4];
-        slab_to_frags<E>(d[it], qf, true);
+        slab_to_frags<E>(d[it], qf, false);
+        phi_q_tile<E>(qf);
         f32x4 nt[4] = {zero4(), zero4(), zero4(), zero4()};
         f32x4 dt = zero4();
         state_read<E>(so, qf, nt, dt);
