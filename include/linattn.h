@@ -44,10 +44,13 @@
  *   - Validation happens on the host before anything is enqueued; a call that
  *     returns an error has written no device memory.
  *   - The library allocates no device memory and keeps none between calls.
- *     Scratch space is the caller's `workspace`.
+ *     Scratch space is the caller's `workspace`, except for
+ *     linattn_forward_noalloc, whose scratch is a static device array that
+ *     every device holds from load to process end.
  *   - The library is reentrant.  Its only global state is a per-thread error
- *     message, a per-device attribute cache, the segment-count override of
- *     linattn_set_segments and the optional kernel timer.
+ *     message, a per-device attribute cache, the per-device address of that
+ *     static scratch, the segment-count override of linattn_set_segments and
+ *     the optional kernel timer.
  *   - No C++ exception crosses this interface.
  */
 #ifndef LINATTN_H
@@ -111,6 +114,27 @@ size_t linattn_forward_workspace_bytes(int B, int H, int N, int C, int M, linatt
 linattn_status linattn_forward(const void *Q, const void *K, const void *V, void *O, int B, int H, int N,
                                int C, int M, linattn_dtype dt, int causal, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/*
+ * linattn_forward_noalloc -- linattn_forward for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  It allocates nothing: the
+ * scratch space linattn_forward takes from `workspace` (the per-segment state
+ * records) is a static device array of LINATTN_NOALLOC_SCRATCH_BYTES inside
+ * the library, one per device, held until the process ends.
+ *
+ * Arguments and results as linattn_forward (bit-identical outputs), without
+ * the workspace.  A problem whose plan needs more scratch than that
+ * (linattn_forward_workspace_bytes(...) > LINATTN_NOALLOC_SCRATCH_BYTES)
+ * returns LINATTN_ERR_WORKSPACE and enqueues nothing.  Every call on a device
+ * shares that device's scratch: calls that overlap on one device (other
+ * streams, other host threads) race and must be serialised by the caller.
+ * The scratch needs no clearing between calls (every record is written
+ * before it is read).  Errors otherwise as linattn_forward.
+ */
+#define LINATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+linattn_status linattn_forward_noalloc(const void *Q, const void *K, const void *V, void *O, int B, int H, int N,
+                                       int C, int M, linattn_dtype dt, int causal, void *stream);
 
 /*
  * linattn_forward_state -- causal forward that starts from a given state and

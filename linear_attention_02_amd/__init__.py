@@ -25,7 +25,7 @@ import os
 import re
 from typing import Optional, Tuple
 
-__all__ = ["forward", "forward_state", "backward", "decode_step", "decode_step_strided", "workspace_bytes",
+__all__ = ["forward", "forward_noalloc", "forward_state", "backward", "decode_step", "decode_step_strided", "workspace_bytes",
            "state_workspace_bytes", "backward_workspace_bytes", "lib", "LinattnError", "timer", "set_segments",
            "plan_segments", "LIB_PATH", "HEADER_PATH"]
 
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.linattn_forward_state_workspace_bytes.argtypes = [i, i, i, i, i, i]
         L.linattn_forward.restype = i
         L.linattn_forward.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
+        L.linattn_forward_noalloc.restype = i
+        L.linattn_forward_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
         L.linattn_forward_state.restype = i
         L.linattn_forward_state.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]
         L.linattn_backward_workspace_bytes.restype = sz
@@ -227,6 +229,21 @@ def forward(q, k, v, causal: bool = True, out=None, workspace=None, stream=None)
     ws = _alloc_ws(nbytes, q.device, workspace)
     _call(q.device, lib().linattn_forward, _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, C, M, dt,
           int(bool(causal)), _ptr(ws), nbytes, _stream(stream, q.device))
+    return out
+
+
+def forward_noalloc(q, k, v, causal: bool = True, out=None, stream=None):
+    """``forward`` through linattn_forward_noalloc: the library's static device
+    scratch instead of a workspace (nothing is allocated when ``out`` is given)."""
+    torch = _torch()
+    B, H, N, C, M = _shape(q, k, v)
+    dt = _dt(q)
+    _check_like("out", out, v)
+    _check_cuda(q, k, v, out)
+    if out is None:
+        out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    _call(q.device, lib().linattn_forward_noalloc, _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, C, M, dt,
+          int(bool(causal)), _stream(stream, q.device))
     return out
 
 

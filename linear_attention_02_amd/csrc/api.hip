@@ -346,6 +346,40 @@ __global__ void state_copy_kernel(const float *S0, const float *z0, float *S_out
   if (i < heads * 64) z_out[i] = z0 ? z0[i] : 0.f;
 }
 
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Scratch of linattn_forward_noalloc: the forward's segment records live in
+// this file-scope device array instead of a caller's workspace.  Every device
+// the library runs on holds its own copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, not a device address: the device
+// address of each device's copy comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is passed on.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[LINATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+linattn_status scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_status(LINATTN_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return set_status(LINATTN_ERR_ARG, "device index beyond the library's table");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return set_status(LINATTN_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LINATTN_OK;
+}
+
 linattn_status forward_impl(const void *Q, const void *K, const void *V, void *O, int B, int H, int N, int C, int M,
                             linattn_dtype dt, int causal, const float *S0, const float *z0, float *S_out,
                             float *z_out, void *workspace, size_t workspace_bytes, void *stream) {
@@ -436,6 +470,28 @@ linattn_status linattn_forward_state(const void *Q, const void *K, const void *V
                                      float *z_out, void *workspace, size_t workspace_bytes, void *stream) {
   try {
     return forward_impl(Q, K, V, O, B, H, N, C, M, dt, 1, S0, z0, S_out, z_out, workspace, workspace_bytes, stream);
+  } catch (...) {
+    return set_status(LINATTN_ERR_ARG, "internal exception");
+  }
+}
+
+linattn_status linattn_forward_noalloc(const void *Q, const void *K, const void *V, void *O, int B, int H, int N,
+                                       int C, int M, linattn_dtype dt, int causal, void *stream) {
+  try {
+    void *ws = nullptr;
+    if (B > 0 && H > 0 && N > 0 && C == 64 && M == 64 && dtype_bytes(dt) != 0) {
+      const Plan plan = plan_forward((long long)B * H, N, causal ? 1 : 0, compute_units(), g_segment_override.load());
+      if (plan.workspace_bytes != SIZE_MAX && plan.workspace_bytes > (size_t)LINATTN_NOALLOC_SCRATCH_BYTES)
+        return set_status(LINATTN_ERR_WORKSPACE, "this problem needs " + std::to_string(plan.workspace_bytes) +
+                                                     " bytes of scratch; the static scratch holds " +
+                                                     std::to_string((size_t)LINATTN_NOALLOC_SCRATCH_BYTES));
+      if (plan.workspace_bytes > 0 && plan.workspace_bytes != SIZE_MAX) {
+        const linattn_status st = scratch_address(&ws);
+        if (st != LINATTN_OK) return st;
+      }
+    }
+    return forward_impl(Q, K, V, O, B, H, N, C, M, dt, causal ? 1 : 0, nullptr, nullptr, nullptr, nullptr, ws,
+                        ws ? (size_t)LINATTN_NOALLOC_SCRATCH_BYTES : 0, stream);
   } catch (...) {
     return set_status(LINATTN_ERR_ARG, "internal exception");
   }

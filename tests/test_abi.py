@@ -188,3 +188,21 @@ def test_host_validation_under_sanitizers():
                            env=dict(os.environ, ASAN_OPTIONS="detect_leaks=1"))
         assert r.returncode == 0, r.stdout + r.stderr
         assert "all host validation checks passed" in r.stdout
+
+
+def test_noalloc_forward_rejects_on_the_host(L):
+    # Validation before any device work: bad arguments as linattn_forward,
+    # and a plan that needs more than the static scratch.
+    nf = lambda **kw: L.linattn_forward_noalloc(*(kw.get(a, d) for a, d in (
+        ("Q", 16), ("K", 32), ("V", 48), ("O", 64), ("B", 1), ("H", 1), ("N", 64), ("C", 64), ("M", 64),
+        ("dt", 1), ("causal", 1))), None)
+    assert nf(Q=None) == NULL
+    assert nf(C=32) == SHAPE
+    assert nf(dt=5) == DTYPE
+    assert nf(Q=17) == ALIGN
+    # 4096 heads, non-causal: two 16,640-byte records per head, 136 MB.
+    need = L.linattn_forward_workspace_bytes(64, 64, 64, 64, 64, 1, 0)
+    assert need > (32 << 20)
+    assert nf(B=64, H=64, N=64, causal=0) == WORKSPACE
+    assert "static scratch" in L.linattn_last_error().decode()
+    assert nf(B=0) == OK
