@@ -13,7 +13,8 @@ inputs resident in HBM.  The same run also times
   * the recurrent decode step on 256 sequences x 8 heads for 3072 steps
     (captured in one HIP graph, one kernel per step), and on 8x the heads,
   * the causal forward on B=16, H=8, N=3072 and the non-causal forward on
-    B=8, H=8, N=4096, warm and cold,
+    B=8, H=8, N=4096, warm and cold, and the fp32 B=1, H=1, N=256 forward
+    (host-inclusive, device-only from a HIP graph replay, and cold),
   * the backward (dQ, dK, dV) of the headline and CIFAR-shaped workloads,
   * forward and forward+backward time and peak memory for N = 2^9..2^16,
   * images/s of greedy generation with a random-weight 12-layer shell
@@ -22,7 +23,8 @@ inputs resident in HBM.  The same run also times
     (`cpu_baseline`, rank 0 only).
 `roofline` is for the dominant kernel (the causal walk): algorithmic bytes
 per launch over its average duration from HIP events recorded on the launch
-stream during the timed steps.  `traffic` comes from the committed
+stream during the timed steps; `roofline.whole_call` puts the same bytes over
+the whole call.  `traffic` comes from the committed
 rocprofv3 FETCH_SIZE / WRITE_SIZE summary when it was taken on the current
 kernel sources, else null.
 """
@@ -41,6 +43,7 @@ if ROOT not in sys.path:
 METRIC = "causal linear-attn fwd tokens/s + % HBM/MFMA roofline; decode tokens/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
+F32_MFMA_PEAK_TFLOPS = 157.3    # dense fp32 matrix
 CSRC = os.path.join(ROOT, "linear_attention_02_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -185,6 +188,85 @@ def time_forward_cold(la, torch, w, iters=20):
     del q, k, v, out, ws, scrub
     return {"median_ms": times[len(times) // 2], "min_ms": times[0], "iters": iters,
             "protocol": "512 MB scrub read before each timed call"}
+
+
+def small_call_record(la, torch, w, steps=200):
+    """A small forward (the fp32 B=1, H=1, N=256 workload): time per call of
+    back-to-back Python calls (host-inclusive), device time per call from one
+    replay of a HIP graph holding `steps` calls, and single cold calls."""
+    from workloads import forward_inputs
+    q, k, v = (t.cuda() for t in forward_inputs(w))
+    out = torch.empty_like(v)
+    ws = torch.empty(max(la.workspace_bytes(w.B, w.H, w.N, q.dtype, w.causal), 1), dtype=torch.uint8, device="cuda")
+
+    def call():
+        la.forward(q, k, v, causal=w.causal, out=out, workspace=ws)
+
+    for _ in range(10):
+        call()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        call()
+    end.record()
+    torch.cuda.synchronize()
+    eager_ms = start.elapsed_time(end) / steps
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for _ in range(steps):
+            call()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    start.record()
+    graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    graph_ms = start.elapsed_time(end) / steps
+    del graph
+    cold = time_forward_cold(la, torch, w)
+    eb = 2 if w.dtype == "bf16" else 4
+    head_tokens = w.B * w.H * w.N
+    alg_bytes = head_tokens * 4 * 64 * eb
+    alg_flops = head_tokens * 4 * 64 * 64
+    peak = F32_MFMA_PEAK_TFLOPS if w.dtype == "f32" else BF16_MFMA_PEAK_TFLOPS
+    return {"workload": w.name, "segments_per_head": la.plan_segments(w.B, w.H, w.N, q.dtype, w.causal),
+            "us_per_call_eager": 1000.0 * eager_ms, "us_per_call_device": 1000.0 * graph_ms,
+            "tokens_per_s_eager": w.tokens / (eager_ms / 1000.0),
+            "tokens_per_s_device": w.tokens / (graph_ms / 1000.0),
+            "cold_us_median": 1000.0 * cold["median_ms"], "tokens_per_s_cold": w.tokens / (cold["median_ms"] / 1000.0),
+            "algorithmic_bytes": alg_bytes, "frac_hbm_device": alg_bytes / (graph_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "alg_TFLOPs_device": alg_flops / (graph_ms * 1e-3) / 1e12,
+            "frac_mfma_peak_device": alg_flops / (graph_ms * 1e-3) / 1e12 / peak,
+            "mfma_peak_TFLOPs": peak,
+            "note": "eager: back-to-back Python calls (includes the binding's host time); device: one replay of a "
+                    "HIP graph holding the calls; cold: single calls after a 512 MB scrub read; a launch-latency-"
+                    "bound size, far below any roofline"}
+
+
+def time_decode_kernel(la, torch, w, steps=256):
+    """Average duration of the decode kernel alone (library HIP events around
+    each launch) over `steps` eager steps on the workload's heads."""
+    from workloads import decode_inputs
+    S = torch.zeros((w.heads, w.C, w.M), dtype=torch.float32, device="cuda")
+    z = torch.zeros((w.heads, w.C), dtype=torch.float32, device="cuda")
+    out = torch.empty((w.heads, w.M), dtype=torch.float32, device="cuda")
+    inputs = [tuple(x.cuda() for x in decode_inputs(w, t)) for t in range(8)]
+    for t in range(4):
+        la.decode_step(S, z, *inputs[t % 8], out=out)
+    torch.cuda.synchronize()
+    la.timer.reset()
+    la.timer.enable(True)
+    for t in range(steps):
+        la.decode_step(S, z, *inputs[t % 8], out=out)
+    torch.cuda.synchronize()
+    la.timer.enable(False)
+    ms, n = la.timer.read(f"decode_step_{w.dtype}")
+    del S, z, out, inputs
+    return 1000.0 * ms / max(n, 1)
 
 
 def time_backward(la, torch, w, steps, warmup):
@@ -492,7 +574,11 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": dom_us},
+                     "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": dom_us,
+                     "whole_call": {"what": "the same algorithmic bytes over the whole forward call "
+                                            "(every kernel of the call and the gaps between them)",
+                                    "achieved": alg_bytes / (ms * 1e-3) / 1e9,
+                                    "frac": alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "ms": ms}},
         "forward_call": {"achieved_GBs": alg_bytes / (ms * 1e-3) / 1e9,
                          "frac_hbm": alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                          "alg_TFLOPs": alg_flops / (ms * 1e-3) / 1e12,
@@ -521,6 +607,10 @@ def main():
                            "frac_hbm": nbytes / (nms * 1e-3) / 1e9 / HBM_PEAK_GBS, "kernels": nk,
                            "warm_note": "ms is back-to-back (inputs may stay in the last-level cache)",
                            "cold": cold}
+    if not args.no_noncausal:
+        w1 = WORKLOADS["causal_f32_b1h1n256"]
+        log(f"forward {w1.name}")
+        result["config_1"] = small_call_record(la, torch, w1)
     if not args.no_backward:
         result["backward"] = {}
         for name in (w.name, "causal_bf16_b16h8n3072", "noncausal_bf16_b8h8n4096"):
@@ -557,6 +647,9 @@ def main():
                             "bytes_per_step": state_bytes + io_bytes,
                             "note": "one kernel per step, 3072 launches replayed from one HIP graph; the 34 MB "
                                     "state can stay in the MI355X's 256 MB last-level cache between steps"}
+        kus = time_decode_kernel(la, torch, wd)
+        result["decode"]["kernel_only_us"] = kus
+        result["decode"]["kernel_only_state_GBs"] = state_bytes / (kus * 1e-6) / 1e9
         # The same step with 8x the sequences: 272 MB of state, more than the
         # last-level cache holds, so every step moves it through HBM.
         from workloads import DecodeWorkload
@@ -565,8 +658,10 @@ def main():
         total_c = time_decode(la, torch, wc, wc.steps)
         per_c = total_c / wc.steps
         sb = wc.heads * (wc.C * wc.M + wc.C) * 4 * 2
+        kc = time_decode_kernel(la, torch, wc, steps=64)
         result["decode"]["cold"] = {"workload": wc.name, "heads": wc.heads, "steps": wc.steps,
-                                    "us_per_step": per_c * 1000.0,
+                                    "us_per_step": per_c * 1000.0, "kernel_only_us": kc,
+                                    "kernel_only_frac_hbm_state": sb / (kc * 1e-6) / 1e9 / HBM_PEAK_GBS,
                                     "tokens_per_s": wc.sequences * wc.steps / (total_c / 1000.0),
                                     "state_GBs": sb / (per_c * 1e-3) / 1e9,
                                     "frac_hbm_state": sb / (per_c * 1e-3) / 1e9 / HBM_PEAK_GBS}

@@ -21,6 +21,8 @@
 
 using namespace linattn;
 
+static_assert(kPlanGroupWaves == kGroupWaves, "planner and kernels agree on the workgroup size");
+
 namespace {
 
 thread_local char g_error[512] = {0};
@@ -139,6 +141,15 @@ void launch_scan(const FwdParams &p, int mode, hipStream_t stream) {
   }
 }
 
+// Non-causal pass 1: one workgroup per kGroupWaves segments of a head.
+template <class E> void launch_group_totals(const FwdParams &p, const Plan &plan, hipStream_t stream) {
+  const size_t pass_bytes = (size_t)plan.heads * (size_t)p.N * 2 * kD * sizeof(E);
+  const auto fn = std::is_same<E, __bf16>::value && pass_bytes > kLastLevelCacheBytes
+                      ? group_totals_kernel<E, kLoadStreaming>
+                      : group_totals_kernel<E, kLoadDefault>;
+  hipLaunchKernelGGL(fn, dim3((unsigned)plan.heads * (unsigned)plan.groups), dim3(64 * kGroupWaves), 0, stream, p);
+}
+
 // Causal passes with at most this many segments per head skip the prefix
 // (suffix) scan: each walk wave sums the totals records it needs.
 bool sum_in_walk(int segments) { return segments <= kSumInWalkMaxSegments; }
@@ -184,20 +195,14 @@ linattn_status run_forward(const FwdParams &base, const Plan &plan, int causal, 
     if (launch_error("causal_walk") != LINATTN_OK) return LINATTN_ERR_HIP;
   } else {
     {
-      TimerScope t(kname("seg_totals", dt), stream);
-      hipLaunchKernelGGL(totals_kernel<E>(plan.heads, p.N), dim3(heads * (unsigned)plan.segments), dim3(64), 0, stream, p,
-                         plan.segments);
+      TimerScope t(kname("group_totals", dt), stream);
+      launch_group_totals<E>(p, plan, stream);
     }
-    if (launch_error("seg_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
-    {
-      TimerScope t("scan", stream);
-      launch_scan(p, kScanTotal, stream);
-    }
-    if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
+    if (launch_error("group_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
     {
       TimerScope t(kname("noncausal_read", dt), stream);
-      hipLaunchKernelGGL(noncausal_read_kernel<E>, dim3(heads * (unsigned)plan.ranges), dim3(64), 0, stream, p,
-                         plan.ranges, plan.range_chunks);
+      hipLaunchKernelGGL(noncausal_read_kernel<E>, dim3(heads * (unsigned)plan.range_groups), dim3(64 * kGroupWaves), 0,
+                         stream, p, plan.groups, plan.ranges, plan.range_chunks);
     }
     if (launch_error("noncausal_read") != LINATTN_OK) return LINATTN_ERR_HIP;
   }
@@ -275,15 +280,20 @@ linattn_status run_backward(const BwdParams &base, const BwdPlan &bp, int causal
     }
     if (launch_error("bwd_walk_r") != LINATTN_OK) return LINATTN_ERR_HIP;
   } else {
+    // The head's (S, z) total is record `groups` of wsF: written by the
+    // forward's read pass, or here by a total scan over the group records.
+    p.segments = plan.groups;
     if (!records_ready) {
       {
-        TimerScope t(kname("seg_totals", dt), stream);
-        hipLaunchKernelGGL(totals_kernel<E>(plan.heads, p.N), dim3(heads * P), dim3(64), 0, stream, f, (int)P);
+        TimerScope t(kname("group_totals", dt), stream);
+        launch_group_totals<E>(f, plan, stream);
       }
-      if (launch_error("seg_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
+      if (launch_error("group_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
+      FwdParams ft = f;
+      ft.segments = plan.groups;
       {
         TimerScope t("scan", stream);
-        launch_scan(f, kScanTotal, stream);
+        launch_scan(ft, kScanTotal, stream);
       }
       if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
     }

@@ -477,25 +477,20 @@ __device__ inline void store_rows(E *Oh, long long row0, int rows_left, const f3
 // ---------------------------------------------------------------------------
 // Pass 1: per-segment totals of phi(K)^T V and phi(K).
 // ---------------------------------------------------------------------------
-template <class E, int kPolicy = kLoadDefault>
-__global__ __launch_bounds__(64, 1) void seg_totals_kernel(FwdParams p, int total_segments) {
-  const int worker = blockIdx.x;
-  const int h = worker % p.heads;
-  const int s = worker / p.heads;
-  if (s >= total_segments) return;
-  const int lane = threadIdx.x;
-  const int n16 = lane & 15, g = lane >> 4;
-  const long long base = (long long)h * p.N * kD;
-  const E *Kh = reinterpret_cast<const E *>(p.K) + base;
-  const E *Vh = reinterpret_cast<const E *>(p.V) + base;
-  const long long t_begin = (long long)s * p.seg_chunks * kChunk;
-  long long t_end = t_begin + (long long)p.seg_chunks * kChunk;
-  if (t_end > p.N) t_end = p.N;
+// LDS staging of one totals wave: K and V of one 64-token chunk (bf16: 16 KB;
+// fp32: 32 KB), as 16-byte vectors.
+template <class E> struct TotalsSlot;
+template <> struct TotalsSlot<__bf16> { static constexpr int kVec = Slot<2>::kVec; };
+template <> struct TotalsSlot<float> { static constexpr int kVec = 2 * 16 * 4 * 16; };
 
-  State st;
+// st = phi(K)^T V and the column sums of phi(K) over tokens [t_begin, t_end)
+// of one head, streamed through the wave's slot.
+template <class E, int kPolicy>
+__device__ inline void range_totals(State &st, u32x4 *slot, const E *Kh, const E *Vh, long long t_begin,
+                                    long long t_end, int lane) {
+  const int n16 = lane & 15, g = lane >> 4;
   state_zero(st);
   if constexpr (std::is_same<E, __bf16>::value) {
-    __shared__ u32x4 slot[Slot<2>::kVec];
     const __bf16 *src[2] = {Kh, Vh};
     stream_lds<2, 0, kPolicy>(slot, src, t_begin, t_end, n16, g, [&](const u32x4 *sl, long long t0, int rows) {
       Frag<E> kt[4][4], vt[4][4];
@@ -529,7 +524,6 @@ __global__ __launch_bounds__(64, 1) void seg_totals_kernel(FwdParams p, int tota
     // chunk's loads in flight while this one is computed.
     const Frag<E> ident = frag_identity<E>(n16, g);
     constexpr int NT = 4;
-    __shared__ u32x4 slot[2 * 16 * NT * 16];
     const float *src[2] = {Kh, Vh};
     if (t_begin < t_end) stage_issue_f32<2, NT>(slot, src, t_begin, chunk_rows(t_begin, t_end), lane);
     for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
@@ -556,8 +550,72 @@ __global__ __launch_bounds__(64, 1) void seg_totals_kernel(FwdParams p, int tota
       state_update<E>(st, kt, vt);
     }
   }
+}
+
+template <class E, int kPolicy = kLoadDefault>
+__global__ __launch_bounds__(64, 1) void seg_totals_kernel(FwdParams p, int total_segments) {
+  const int worker = blockIdx.x;
+  const int h = worker % p.heads;
+  const int s = worker / p.heads;
+  if (s >= total_segments) return;
+  const int lane = threadIdx.x;
+  const int n16 = lane & 15, g = lane >> 4;
+  const long long base = (long long)h * p.N * kD;
+  const long long t_begin = (long long)s * p.seg_chunks * kChunk;
+  long long t_end = t_begin + (long long)p.seg_chunks * kChunk;
+  if (t_end > p.N) t_end = p.N;
+  __shared__ u32x4 slot[TotalsSlot<E>::kVec];
+  State st;
+  range_totals<E, kPolicy>(st, slot, reinterpret_cast<const E *>(p.K) + base, reinterpret_cast<const E *>(p.V) + base,
+                           t_begin, t_end, lane);
   float *rec = p.ws + ((long long)h * p.records + s) * kStateFloats;
   state_store_record(st, rec, lane, n16, g);
+}
+
+// ---------------------------------------------------------------------------
+// Non-causal pass 1 in workgroups: kGroupWaves waves of one head take
+// consecutive segments, and their partial states meet in the LDS (the
+// staging slots, free once the chunks are consumed), where they are added in
+// wave order and written as one record per group.  The head's total is the
+// sum of its `groups` records, in record order, which the read pass forms
+// itself: no scan launch.
+// ---------------------------------------------------------------------------
+constexpr int kGroupWaves = 4;
+constexpr int kStateVecs = kStateFloats / 4;
+
+template <class E> struct GroupSlot {
+  static constexpr int kVec = TotalsSlot<E>::kVec > kStateVecs ? TotalsSlot<E>::kVec : kStateVecs;
+};
+
+template <class E, int kPolicy = kLoadDefault>
+__global__ __launch_bounds__(64 * kGroupWaves, 1) void group_totals_kernel(FwdParams p) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n16 = lane & 15, g = lane >> 4;
+  const int h = blockIdx.x % p.heads;
+  const int grp = blockIdx.x / p.heads;
+  const int s = grp * kGroupWaves + wave;
+  __shared__ u32x4 slots[kGroupWaves][GroupSlot<E>::kVec];
+  State st;
+  if (s < p.segments) {
+    const long long base = (long long)h * p.N * kD;
+    const long long t_begin = (long long)s * p.seg_chunks * kChunk;
+    long long t_end = t_begin + (long long)p.seg_chunks * kChunk;
+    if (t_end > p.N) t_end = p.N;
+    range_totals<E, kPolicy>(st, slots[wave], reinterpret_cast<const E *>(p.K) + base,
+                             reinterpret_cast<const E *>(p.V) + base, t_begin, t_end, lane);
+  } else {
+    state_zero(st);
+  }
+  wait_vmcnt<0>();
+  state_store_record(st, reinterpret_cast<float *>(slots[wave]), lane, n16, g);
+  __syncthreads();
+  f32x4 *rec = reinterpret_cast<f32x4 *>(p.ws + ((long long)h * p.records + grp) * kStateFloats);
+  for (int v = threadIdx.x; v < kStateVecs; v += 64 * kGroupWaves) {
+    f32x4 a = __builtin_bit_cast(f32x4, slots[0][v]);
+#pragma unroll
+    for (int w = 1; w < kGroupWaves; ++w) a += __builtin_bit_cast(f32x4, slots[w][v]);
+    rec[v] = a;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -970,32 +1028,65 @@ template <> struct WalkKernel<float> { static constexpr auto fn = causal_walk_ke
 
 // ---------------------------------------------------------------------------
 // Non-causal pass 2: o_i = phi(q_i)^T S / phi(q_i)^T z with the head's total
-// S, z (record `segments` of the workspace) -- "Why Replace Attention?",
-// §6.2 -- for one range of chunks per wave.
+// S, z -- "Why Replace Attention?", §6.2 -- in workgroups of kGroupWaves
+// waves of one head, one range of chunks per wave.  The workgroup first sums
+// the head's `groups` records (in record order; the first workgroup of each
+// head also stores that total as record `groups`, for a backward that reuses
+// it), each wave's first chunk of Q already on its way.
 // ---------------------------------------------------------------------------
+template <class E> struct ReadSlot;
+template <> struct ReadSlot<__bf16> { static constexpr int kVec = Slot<1>::kVec; };
+template <> struct ReadSlot<float> { static constexpr int kVec = 16 * 4 * 16; };
+
+// tot = sum of the head's `groups` records (16-byte vectors split over the
+// workgroup's threads).
+__device__ inline void sum_group_records(u32x4 *tot, const FwdParams &p, int h, int groups, bool store_total) {
+  const f32x4 *recs = reinterpret_cast<const f32x4 *>(p.ws + (long long)h * p.records * kStateFloats);
+  f32x4 *total = reinterpret_cast<f32x4 *>(p.ws + ((long long)h * p.records + groups) * kStateFloats);
+  for (int v = threadIdx.x; v < kStateVecs; v += 64 * kGroupWaves) {
+    f32x4 a = recs[v];
+    for (int j = 1; j < groups; ++j) a += recs[(long long)j * kStateVecs + v];
+    tot[v] = __builtin_bit_cast(u32x4, a);
+    if (store_total) total[v] = a;
+  }
+}
+
 template <class E>
-__global__ __launch_bounds__(64, 1) void noncausal_read_kernel(FwdParams p, int ranges, int range_chunks) {
-  const int worker = blockIdx.x;
-  const int h = worker % p.heads;
-  const int s = worker / p.heads;
-  if (s >= ranges) return;
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(64 * kGroupWaves, 1) void noncausal_read_kernel(FwdParams p, int groups, int ranges,
+                                                                              int range_chunks) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n16 = lane & 15, g = lane >> 4;
+  const int h = blockIdx.x % p.heads;
+  const int rg = blockIdx.x / p.heads;
+  const int s = rg * kGroupWaves + wave;
   const long long base = (long long)h * p.N * kD;
   const E *Qh = reinterpret_cast<const E *>(p.Q) + base;
   E *Oh = reinterpret_cast<E *>(p.O) + base;
-  const long long t_begin = (long long)s * range_chunks * kChunk;
+  long long t_begin = (long long)s * range_chunks * kChunk;
   long long t_end = t_begin + (long long)range_chunks * kChunk;
   if (t_end > p.N) t_end = p.N;
+  if (s >= ranges) t_begin = t_end = 0;  // no range: takes part in the sum only
+
+  __shared__ u32x4 slots[kGroupWaves][ReadSlot<E>::kVec];
+  __shared__ u32x4 tot[kStateVecs];
+  u32x4 *slot = slots[wave];
+  if constexpr (std::is_same<E, __bf16>::value) {
+    const __bf16 *src[1] = {Qh};
+    if (t_begin < t_end) stage_issue<1>(slot, src, t_begin, chunk_rows(t_begin, t_end), n16, g);
+  } else {
+    const float *src[1] = {Qh};
+    if (t_begin < t_end) stage_issue_f32<1, 4>(slot, src, t_begin, chunk_rows(t_begin, t_end), lane);
+  }
+  sum_group_records(tot, p, h, groups, rg == 0);
+  __syncthreads();
+  if (t_begin >= t_end) return;
 
   State st;
-  state_load_record(st, p.ws + ((long long)h * p.records + p.segments) * kStateFloats, lane, g);
+  state_load_record(st, reinterpret_cast<const float *>(tot), lane, g);
   StateOperands<E> so;
   state_operands<E>(st, so);
   if constexpr (std::is_same<E, __bf16>::value) {
-    __shared__ u32x4 slot[Slot<1>::kVec];
     const __bf16 *src[1] = {Qh};
-    if (t_begin < t_end) stage_issue<1>(slot, src, t_begin, chunk_rows(t_begin, t_end), n16, g);
     for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
       const int rows = chunk_rows(t0, t_end);
       if (t0 == t_begin) {  // see stream_lds
@@ -1022,9 +1113,7 @@ __global__ __launch_bounds__(64, 1) void noncausal_read_kernel(FwdParams p, int 
     // loads in flight while this one is computed.
     constexpr int NT = 4;
     constexpr int kStores = 4 * NT;  // output stores of a full chunk
-    __shared__ u32x4 slot[16 * NT * 16];
     const float *src[1] = {Qh};
-    if (t_begin < t_end) stage_issue_f32<1, NT>(slot, src, t_begin, chunk_rows(t_begin, t_end), lane);
     for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
       const int rows = chunk_rows(t0, t_end);
       if (t0 == t_begin) {  // see stream_lds

@@ -26,6 +26,7 @@ constexpr long long kMaxShortSegments = 64;
 // holds about 480 registers per lane).
 constexpr long long kWavesPerCU = 4;
 
+
 Check fail(linattn_status s, const std::string &msg) {
   Check c;
   c.status = s;
@@ -89,13 +90,17 @@ Plan plan_forward(long long heads, long long N, int causal, int cus, int overrid
   if (causal) {
     p.records = p.segments > 1 ? p.segments : 0;
   } else {
-    p.records = p.segments + 1;  // partial totals, then the head's total
+    // Segments are summed in workgroups of kPlanGroupWaves; one record per group,
+    // then the head's total.
+    p.groups = (int)ceil_div(p.segments, kPlanGroupWaves);
+    p.records = p.groups + 1;
     long long ranges = ceil_div(target, heads);
     if (ranges > p.chunks) ranges = p.chunks;
     if (ranges < 1) ranges = 1;
     long long range_chunks = ceil_div(p.chunks, ranges);
     p.ranges = (int)ceil_div(p.chunks, range_chunks);
     p.range_chunks = (int)range_chunks;
+    p.range_groups = (int)ceil_div(p.ranges, kPlanGroupWaves);
   }
   size_t bytes = 0;
   if (!mul3((size_t)heads, (size_t)p.records, kStateBytes, &bytes)) bytes = SIZE_MAX;

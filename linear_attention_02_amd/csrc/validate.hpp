@@ -28,14 +28,21 @@ struct Check {
 size_t dtype_bytes(linattn_dtype dt);  // 0 for an unknown type
 
 // Launch plan for one forward call.
+// Waves per workgroup of the non-causal kernels: one head's consecutive
+// segments (ranges) share a workgroup.
+constexpr int kPlanGroupWaves = 4;
+
 struct Plan {
   long long heads = 0;      // B * H
   long long chunks = 0;     // ceil(N / 64)
   int segments = 1;         // sequence segments per head (scan units)
   int seg_chunks = 0;       // chunks per segment
   int records = 0;          // state records per head in the workspace
+  int groups = 0;           // non-causal: totals workgroups per head (records 0..groups-1; the
+                            // head's total is record `groups`)
   int ranges = 0;           // non-causal read ranges per head
   int range_chunks = 0;     // chunks per read range
+  int range_groups = 0;     // non-causal read workgroups per head
   size_t workspace_bytes = 0;
 };
 

@@ -28,7 +28,13 @@ int main() {
   p = plan_forward(128, 3072, 1, 256, 0);
   EXPECT(p.segments == 8 && p.seg_chunks == 6);
   p = plan_forward(64, 4096, 0, 256, 0);
-  EXPECT(p.segments == 16 && p.records == 17 && p.ranges == 16 && p.range_chunks == 4);
+  // Non-causal: 16 segments summed by 4 workgroups (one record each), then the total.
+  EXPECT(p.segments == 16 && p.groups == 4 && p.records == 5 && p.ranges == 16 && p.range_chunks == 4 &&
+         p.range_groups == 4);
+  EXPECT(p.workspace_bytes == (size_t)64 * 5 * 4160 * 4);
+  p = plan_forward(3, 64 * 10, 0, 256, 7);  // 7 segments: groups of 4 and 3
+  EXPECT(p.segments == 5 || p.segments == 7);
+  EXPECT(p.groups == (p.segments + 3) / 4 && p.records == p.groups + 1);
   // Few heads, short sequences: segments shorter than 4 chunks (down to one)
   // where longer ones would leave the device short of waves, at most 64.
   p = plan_forward(1, 65, 1, 256, 0);  // two chunks
