@@ -30,7 +30,9 @@ __all__ = ["forward", "forward_noalloc", "forward_state", "backward", "decode_st
            "plan_segments", "LIB_PATH", "HEADER_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblinattn.so")
+# LINATTN_LIB selects another in-tree build (e.g. the 32-token-chunk walk
+# variant of ``python -m linear_attention_02_amd.build --walk-tiles 2 --out ...``).
+LIB_PATH = os.environ.get("LINATTN_LIB") or os.path.join(_HERE, "liblinattn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "linattn.h")
 
 F32, BF16 = 0, 1

@@ -1,6 +1,6 @@
 """Builds liblinattn.so (HIP, gfx950) in-tree.
 
-    python -m linear_attention_02_amd.build [-v]
+    python -m linear_attention_02_amd.build [-v] [--walk-tiles 2 --out PATH]
 
 Also builds ``validate_host`` objects with the host compiler only when asked
 (``--host-check``), for sanitizer runs of the argument checks without HIP.
@@ -35,9 +35,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False, extra=None) -> str:
-    tmp = LIB + ".tmp"
-    obj_dir = os.path.join(HERE, "_build")
+def build(verbose: bool = False, extra=None, walk_tiles: int = 0, out: str = None) -> str:
+    """Compiles liblinattn.so (or ``out``).  walk_tiles = 2 builds the bf16
+    causal walk with 32-token chunks instead of 64 (a measurement variant)."""
+    lib = out or LIB
+    tmp = lib + ".tmp"
+    obj_dir = os.path.join(HERE, "_build" if not out else "_build_" + os.path.basename(out).replace(".", "_"))
+    extra = list(extra or [])
+    if walk_tiles:
+        extra.append(f"-DLINATTN_WALK_TILES_BF16={int(walk_tiles)}")
     os.makedirs(obj_dir, exist_ok=True)
     api_o = os.path.join(obj_dir, "api.o")
     val_o = os.path.join(obj_dir, "validate.o")
@@ -50,8 +56,8 @@ def build(verbose: bool = False, extra=None) -> str:
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def build_host_check(out_dir: str, sanitize: bool = True) -> str:
@@ -67,4 +73,11 @@ def build_host_check(out_dir: str, sanitize: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv, extra=[a for a in sys.argv[1:] if a.startswith("-R")])
+    import argparse
+    ap = argparse.ArgumentParser(description="Build liblinattn.so for gfx950 in-tree.")
+    ap.add_argument("-v", action="store_true")
+    ap.add_argument("--walk-tiles", type=int, default=0, choices=(0, 2, 4),
+                    help="row tiles per chunk of the bf16 causal walk (2: 32-token chunks; default 4)")
+    ap.add_argument("--out", default=None, help="output path (default: linear_attention_02_amd/liblinattn.so)")
+    args, rest = ap.parse_known_args()
+    build(verbose=args.v, extra=[a for a in rest if a.startswith("-R")], walk_tiles=args.walk_tiles, out=args.out)

@@ -911,10 +911,16 @@ __device__ inline void causal_chunk_lds(State &st, u32x4 *slot, const __bf16 *co
   causal_chunk<E, NT, kFull>(st, qf, kf, kt, vt, rows, Oh, t0, n16, g);
 }
 
-// Row tiles per chunk of the bf16 walk (4: 64-token chunks).  32-token
-// chunks fit two waves per SIMD but were measured slower: the walk is bound
-// by HBM traffic either way, and smaller chunks add per-chunk work.
-constexpr int kWalkTilesBf16 = 4;
+// Row tiles per chunk of the bf16 walk: 4 (64-token chunks, the default) or
+// 2 (32-token chunks, built with -DLINATTN_WALK_TILES_BF16=2).  The 32-token
+// walk fits in 256 registers, so two waves share a SIMD; it was measured
+// slower on MI355X (the walk is bound by memory traffic either way, and
+// smaller chunks add per-chunk work), so 64 is the product default.
+#ifndef LINATTN_WALK_TILES_BF16
+#define LINATTN_WALK_TILES_BF16 4
+#endif
+constexpr int kWalkTilesBf16 = LINATTN_WALK_TILES_BF16;
+static_assert(kWalkTilesBf16 == 2 || kWalkTilesBf16 == 4, "the bf16 walk takes 32- or 64-token chunks");
 
 template <class E>
 __device__ inline void causal_walk(const FwdParams &p) {
@@ -1019,8 +1025,11 @@ __device__ inline void causal_walk(const FwdParams &p) {
 }
 
 // One wave per SIMD: the walk keeps the state, one chunk's fragments and the
-// products' accumulators in registers (about 480 of the 512).
-__global__ __launch_bounds__(64, 1) void causal_walk_kernel_bf16(FwdParams p) { causal_walk<__bf16>(p); }
+// products' accumulators in registers (about 480 of the 512).  With 32-token
+// chunks it is held to 256 registers, two waves per SIMD.
+__global__ __launch_bounds__(64, kWalkTilesBf16 == 2 ? 2 : 1) void causal_walk_kernel_bf16(FwdParams p) {
+  causal_walk<__bf16>(p);
+}
 __global__ __launch_bounds__(64, 1) void causal_walk_kernel_f32(FwdParams p) { causal_walk<float>(p); }
 template <class E> struct WalkKernel;
 template <> struct WalkKernel<__bf16> { static constexpr auto fn = causal_walk_kernel_bf16; };
