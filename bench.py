@@ -335,9 +335,56 @@ def time_train_step(la, torch, w, steps, warmup):
     return ms
 
 
+def time_train_pair(la, torch, w, steps, warmup):
+    """linattn_forward_train then linattn_backward_train: the forward alone,
+    the backward alone (it only reads what the forward saved, so it can be
+    repeated after one forward), the pair per step, and per-kernel times from
+    the library's events (a separate loop)."""
+    from workloads import backward_inputs
+    q, k, v, g = (t.cuda() for t in backward_inputs(w))
+    o = torch.empty_like(v)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(la.train_workspace_bytes(w.B, w.H, w.N, q.dtype, w.causal), 1), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+    fwd = lambda: la.forward_train(q, k, v, causal=w.causal, out=o, workspace=ws, stream=stream)
+    bwd = lambda: la.backward_train(q, k, v, o, g, ws, causal=w.causal, dq=dq, dk=dk, dv=dv, stream=stream)
+
+    def pair():
+        fwd()
+        bwd()
+
+    def timed(fn, with_kernel_events=False) -> float:
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        la.timer.reset()
+        la.timer.enable(with_kernel_events)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(steps):
+            fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        la.timer.enable(False)
+        return start.elapsed_time(end) / steps
+
+    rec = {"forward_ms": timed(fwd), "backward_ms": None, "pair_ms": timed(pair)}
+    fwd()
+    rec["backward_ms"] = timed(bwd)
+    timed(pair, with_kernel_events=True)
+    rec["kernels"] = {}
+    for name in la.timer.names():
+        kms, n = la.timer.read(name)
+        rec["kernels"][name] = {"avg_us": 1000.0 * kms / max(n, 1), "launches": n}
+    del q, k, v, g, o, dq, dk, dv, ws
+    return rec
+
+
 def backward_record(la, torch, w, steps, warmup):
     ms, kernels, ms_events = time_backward(la, torch, w, steps, warmup)
     train_ms = time_train_step(la, torch, w, steps, warmup)
+    train = time_train_pair(la, torch, w, steps, warmup)
     eb = 2 if w.dtype == "bf16" else 4
     head_tokens = w.B * w.H * w.N
     row = 64 * eb
@@ -347,11 +394,21 @@ def backward_record(la, torch, w, steps, warmup):
            "tokens_per_s": w.tokens / (ms / 1000.0), "algorithmic_bytes": alg,
            "achieved_GBs": alg / (ms * 1e-3) / 1e9, "frac_hbm": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
            "kernels": kernels}
+    # The training pair: linattn_backward_train after linattn_forward_train
+    # (bf16 causal: the saved-forward one-pass backward).
+    bt = train["backward_ms"]
+    rec["train_pair"] = dict(train, backward_tokens_per_s=w.tokens / (bt / 1000.0),
+                             backward_frac_hbm=alg / (bt * 1e-3) / 1e9 / HBM_PEAK_GBS)
     # Per-kernel rooflines on the bytes each kernel must move in this design:
     # walk_f reads Q, K, V, dO and writes dQ and one 8-byte pair per token;
     # walk_r reads Q, K, V, dO and the pairs and writes dK, dV.
     per_token = {f"bwd_walk_f_{w.dtype}": 5 * row + 8, f"bwd_walk_r_{w.dtype}": 6 * row + 8,
                  f"bwd_nc_a_{w.dtype}": 3 * row + 8, f"bwd_nc_b_{w.dtype}": 4 * row}
+    # Saved-forward backward: the totals read Q, dO, O and 1/den and write the
+    # pairs (1/den, b); the walk reads Q, K, V, dO and the pairs and writes
+    # dQ, dK, dV.
+    per_token_train = {"bwd_saved_totals_bf16": 3 * row + 4 + 8, "bwd_saved_walk_bf16": 7 * row + 8,
+                       "causal_walk_save_bf16": 4 * row + 4}
     roof = {}
     for name, b in per_token.items():
         if name in kernels:
@@ -360,6 +417,14 @@ def backward_record(la, torch, w, steps, warmup):
             roof[name] = {"bytes_per_launch": head_tokens * b, "avg_launch_us": us, "achieved_GBs": gbs,
                           "frac_hbm": gbs / HBM_PEAK_GBS}
     rec["kernel_rooflines"] = roof
+    troof = {}
+    for name, b in per_token_train.items():
+        if name in train["kernels"]:
+            us = train["kernels"][name]["avg_us"]
+            gbs = head_tokens * b / (us * 1e-6) / 1e9
+            troof[name] = {"bytes_per_launch": head_tokens * b, "avg_launch_us": us, "achieved_GBs": gbs,
+                           "frac_hbm": gbs / HBM_PEAK_GBS}
+    rec["train_pair"]["kernel_rooflines"] = troof
     return rec
 
 

@@ -217,6 +217,57 @@ linattn_status linattn_backward_after_forward(const void *Q, const void *K, cons
                                               linattn_dtype dt, int causal, void *workspace, size_t workspace_bytes,
                                               void *stream);
 
+/* Bytes of device workspace the pair linattn_forward_train /
+ * linattn_backward_train needs (0 for invalid arguments).  At least
+ * linattn_backward_workspace_bytes(...). */
+size_t linattn_train_workspace_bytes(int B, int H, int N, int C, int M, linattn_dtype dt, int causal);
+
+/*
+ * linattn_forward_train -- linattn_forward for a training step: the same
+ * outputs, bit for bit, and it also leaves in `workspace` what
+ * linattn_backward_train reads: the per-segment (S, z) records and, for bf16
+ * causal calls, 1/den_i of every token (den_i = phi(q_i)^T z_i, the
+ * normaliser of "Why Replace Attention?", §5.4), 4 bytes per token.
+ *
+ * workspace: device buffer of at least linattn_train_workspace_bytes(...)
+ *   bytes, 16-byte aligned, disjoint from Q, K, V and O.
+ * Other arguments and errors as linattn_forward.
+ */
+linattn_status linattn_forward_train(const void *Q, const void *K, const void *V, void *O, int B, int H, int N,
+                                     int C, int M, linattn_dtype dt, int causal, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/*
+ * linattn_backward_train -- the gradients of linattn_backward after
+ * linattn_forward_train, reading that forward's output O and saved 1/den_i.
+ * The gradients are the forward and reverse cumulative sums of
+ * "[Paper Review] Transformers are RNNs", §3.5 ("Gradient Computation").
+ *
+ * bf16, causal: with O and 1/den_i the per-token factors a_i = g_i / den_i
+ *   and b_i = -(g_i . o_i) / den_i need no state, so one pass over Q, dO and
+ *   O forms the reverse sums and one left-to-right pass over Q, K, V and dO
+ *   writes dQ, dK and dV together (10 tensor passes of B*H*N*64 elements in
+ *   all, against 13 for linattn_backward_after_forward).  b_i is formed from
+ *   the stored (bf16) O, so the results differ from linattn_backward's in
+ *   rounding only; the error bounds of linattn_backward hold.
+ * fp32, or causal = 0: linattn_backward_after_forward on the records the
+ *   forward left (bit-identical to linattn_backward); O is checked, not read.
+ *
+ * O: [B,H,N,64] in `dt`, the output of that linattn_forward_train call;
+ *   16-byte aligned; must not overlap dQ, dK, dV or the workspace.
+ * Precondition (not checked): the last call that wrote `workspace` was
+ * linattn_forward_train with the same Q, K, V contents, B, H, N, dt and
+ * causal flag, on the same device and segment override, and O is unchanged
+ * since.  With a violated precondition the gradients are wrong; nothing
+ * faults.
+ * Other arguments, errors and results as linattn_backward (ALIAS also when O
+ *   overlaps an output or the workspace).  Deterministic.
+ */
+linattn_status linattn_backward_train(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                                      void *dQ, void *dK, void *dV, int B, int H, int N, int C, int M,
+                                      linattn_dtype dt, int causal, void *workspace, size_t workspace_bytes,
+                                      void *stream);
+
 /*
  * linattn_decode_step -- one constant-state recurrent step for BH independent
  * heads ("Why Replace Attention?", §7.2, steps 1-4; §7.4 constant work per

@@ -82,6 +82,12 @@ def lib() -> ctypes.CDLL:
         L.linattn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
         L.linattn_backward_after_forward.restype = i
         L.linattn_backward_after_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
+        L.linattn_train_workspace_bytes.restype = sz
+        L.linattn_train_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        L.linattn_forward_train.restype = i
+        L.linattn_forward_train.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
+        L.linattn_backward_train.restype = i
+        L.linattn_backward_train.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
         L.linattn_decode_step_strided.restype = i
         L.linattn_decode_step_strided.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, ctypes.c_longlong, vp]
         L.linattn_decode_step.restype = i
@@ -307,6 +313,59 @@ def backward(q, k, v, grad_out, causal: bool = True, dq=None, dk=None, dv=None, 
     fn = lib().linattn_backward_after_forward if after_forward else lib().linattn_backward
     _call(q.device, fn, _ptr(q), _ptr(k), _ptr(v), _ptr(grad_out), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, C, M, dt,
           int(bool(causal)), _ptr(ws), nbytes, _stream(stream, q.device))
+    return dq, dk, dv
+
+
+def train_workspace_bytes(B: int, H: int, N: int, dtype, causal: bool) -> int:
+    dt = F32 if str(dtype).endswith("float32") else BF16
+    return int(lib().linattn_train_workspace_bytes(B, H, N, 64, 64, dt, int(bool(causal))))
+
+
+def forward_train(q, k, v, causal: bool = True, out=None, workspace=None, stream=None):
+    """``forward`` for a training step; returns (o, workspace).
+
+    The workspace (sized by train_workspace_bytes) then holds what
+    ``backward_train`` reads: the segment records and, for bf16 causal calls,
+    1/den per token.  o equals ``forward``'s bit for bit.
+    """
+    torch = _torch()
+    B, H, N, C, M = _shape(q, k, v)
+    dt = _dt(q)
+    _check_like("out", out, v)
+    _check_cuda(q, k, v, out)
+    if out is None:
+        out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    nbytes = int(lib().linattn_train_workspace_bytes(B, H, N, C, M, dt, int(bool(causal))))
+    ws = _alloc_ws(nbytes, q.device, workspace)
+    _call(q.device, lib().linattn_forward_train, _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, C, M, dt,
+          int(bool(causal)), _ptr(ws), nbytes, _stream(stream, q.device))
+    return out, ws
+
+
+def backward_train(q, k, v, o, grad_out, workspace, causal: bool = True, dq=None, dk=None, dv=None, stream=None):
+    """Gradients after ``forward_train`` on the same q, k, v and causal flag,
+    with its output ``o`` and ``workspace``; returns (dq, dk, dv)."""
+    torch = _torch()
+    B, H, N, C, M = _shape(q, k, v)
+    if grad_out.shape != v.shape or grad_out.dtype != v.dtype:
+        raise LinattnError(2, "grad_out must match v in shape and dtype")
+    _check_like("o", o, v)
+    if o is None:
+        raise LinattnError(1, "backward_train needs the forward's output o")
+    dt = _dt(q)
+    _check_like("dq", dq, q)
+    _check_like("dk", dk, k)
+    _check_like("dv", dv, v)
+    _check_cuda(q, k, v, o, grad_out, dq, dk, dv)
+    nbytes = int(lib().linattn_train_workspace_bytes(B, H, N, C, M, dt, int(bool(causal))))
+    if nbytes > 0 and workspace is None:
+        raise LinattnError(8, "backward_train needs the workspace forward_train used")
+    dq = torch.empty(q.shape, dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=k.dtype, device=k.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=v.dtype, device=v.device) if dv is None else dv
+    ws = _alloc_ws(nbytes, q.device, workspace)
+    _call(q.device, lib().linattn_backward_train, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(grad_out), _ptr(dq),
+          _ptr(dk), _ptr(dv), B, H, N, C, M, dt, int(bool(causal)), _ptr(ws), nbytes, _stream(stream, q.device))
     return dq, dk, dv
 
 

@@ -15,6 +15,7 @@
 
 #include "../../include/linattn.h"
 #include "backward_kernels.hpp"
+#include "backward_saved_kernels.hpp"
 #include "decode_kernel.hpp"
 #include "forward_kernels.hpp"
 #include "validate.hpp"
@@ -188,7 +189,10 @@ linattn_status run_forward(const FwdParams &base, const Plan &plan, int causal, 
     } else {
       p.init = p.S0 != nullptr ? kInitNatural : kInitZero;
     }
-    {
+    if (std::is_same<E, __bf16>::value && p.rden != nullptr) {
+      TimerScope t("causal_walk_save_bf16", stream);
+      hipLaunchKernelGGL(causal_walk_save_kernel_bf16, dim3(heads * (unsigned)plan.segments), dim3(64), 0, stream, p);
+    } else {
       TimerScope t(kname("causal_walk", dt), stream);
       hipLaunchKernelGGL(WalkKernel<E>::fn, dim3(heads * (unsigned)plan.segments), dim3(64), 0, stream, p);
     }
@@ -317,6 +321,51 @@ linattn_status run_backward(const BwdParams &base, const BwdPlan &bp, int causal
   return set_status(LINATTN_OK, "");
 }
 
+// The bf16 causal backward after linattn_forward_train: saved totals, the
+// suffix scan of their records (none with at most kSumInWalkMaxSegments
+// segments: the walk sums them), then the one-pass walk.
+linattn_status run_saved_backward(const BwdParams &base, const TrainPlan &tp, hipStream_t stream) {
+  const Plan &plan = tp.bwd.fwd;
+  BwdParams p = base;
+  p.segments = plan.segments;
+  p.seg_chunks = plan.seg_chunks;
+  p.recF = plan.records;
+  p.recT = tp.recT;
+  p.walk_k = tp.walk_k;
+  p.walk_segments = tp.walk_segments;
+  p.rev_segments = tp.rev_segments;
+  p.rev_chunks = tp.rev_chunks;
+  p.sum_in_walk = sum_in_walk(plan.segments) ? 1 : 0;
+  p.rev_sum_in_walk = sum_in_walk(tp.rev_segments) ? 1 : 0;
+  const unsigned heads = (unsigned)plan.heads;
+  {
+    TimerScope t("bwd_saved_totals_bf16", stream);
+    const bool streaming = (size_t)plan.heads * (size_t)p.N * 3 * kD * sizeof(__bf16) > kLastLevelCacheBytes;
+    hipLaunchKernelGGL(streaming ? bwd_saved_totals_kernel<kLoadStreaming> : bwd_saved_totals_kernel<kLoadDefault>,
+                       dim3(heads * (unsigned)tp.rev_segments), dim3(64), 0, stream, p);
+  }
+  if (launch_error("bwd_saved_totals") != LINATTN_OK) return LINATTN_ERR_HIP;
+  if (!p.rev_sum_in_walk) {
+    FwdParams t{};
+    t.N = p.N;
+    t.heads = p.heads;
+    t.segments = tp.recT;
+    t.records = tp.recT;
+    t.ws = p.wsT;
+    {
+      TimerScope ts("scan", stream);
+      launch_scan(t, kScanSuffix, stream);
+    }
+    if (launch_error("scan") != LINATTN_OK) return LINATTN_ERR_HIP;
+  }
+  {
+    TimerScope t("bwd_saved_walk_bf16", stream);
+    hipLaunchKernelGGL(bwd_saved_walk_kernel, dim3(heads * (unsigned)tp.walk_segments), dim3(256), 0, stream, p);
+  }
+  if (launch_error("bwd_saved_walk") != LINATTN_OK) return LINATTN_ERR_HIP;
+  return set_status(LINATTN_OK, "");
+}
+
 linattn_status backward_impl(const void *Q, const void *K, const void *V, const void *dO, void *dQ, void *dK,
                              void *dV, int B, int H, int N, int C, int M, linattn_dtype dt, int causal,
                              bool records_ready, void *workspace, size_t workspace_bytes, void *stream) {
@@ -346,6 +395,73 @@ linattn_status backward_impl(const void *Q, const void *K, const void *V, const 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dt == LINATTN_BF16) return run_backward<__bf16>(p, bp, causal, records_ready, s, dt);
   return run_backward<float>(p, bp, causal, records_ready, s, dt);
+}
+
+linattn_status forward_train_impl(const void *Q, const void *K, const void *V, void *O, int B, int H, int N, int C,
+                                  int M, linattn_dtype dt, int causal, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+  const long long heads = (long long)B * (long long)H;
+  TrainPlan tp;
+  if (B >= 0 && H >= 0 && N >= 0)
+    tp = plan_train(heads, N, causal, (heads > 0 && N > 0) ? compute_units() : 1, g_segment_override.load());
+  const Check c = check_forward(Q, K, V, O, B, H, N, C, M, dt, workspace, workspace_bytes,
+                                (heads > 0 && N > 0) ? tp.workspace_bytes : 0);
+  if (!c.ok()) return from_check(c);
+  if (heads == 0 || N == 0) return set_status(LINATTN_OK, "");
+  FwdParams p{};
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.O = O;
+  p.N = N;
+  p.heads = (int)heads;
+  p.ws = reinterpret_cast<float *>(workspace);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dt == LINATTN_BF16) {
+    if (causal) {
+      p.rden = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + tp.off_rden);
+      p.rden_stride = tp.bwd.stats_stride;
+    }
+    return run_forward<__bf16>(p, tp.bwd.fwd, causal, s, dt);
+  }
+  return run_forward<float>(p, tp.bwd.fwd, causal, s, dt);
+}
+
+linattn_status backward_train_impl(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                                   void *dQ, void *dK, void *dV, int B, int H, int N, int C, int M, linattn_dtype dt,
+                                   int causal, void *workspace, size_t workspace_bytes, void *stream) {
+  const long long heads = (long long)B * (long long)H;
+  TrainPlan tp;
+  if (B >= 0 && H >= 0 && N >= 0)
+    tp = plan_train(heads, N, causal, (heads > 0 && N > 0) ? compute_units() : 1, g_segment_override.load());
+  const Check c = check_backward_train(Q, K, V, O, dO, dQ, dK, dV, B, H, N, C, M, dt, workspace, workspace_bytes,
+                                       (heads > 0 && N > 0) ? tp.workspace_bytes : 0);
+  if (!c.ok()) return from_check(c);
+  if (heads == 0 || N == 0) return set_status(LINATTN_OK, "");
+  BwdParams p{};
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.dO = dO;
+  p.dQ = dQ;
+  p.dK = dK;
+  p.dV = dV;
+  p.N = N;
+  p.heads = (int)heads;
+  char *ws = reinterpret_cast<char *>(workspace);
+  p.wsF = reinterpret_cast<float *>(ws);
+  p.wsR = reinterpret_cast<float *>(ws + tp.bwd.off_r);
+  p.stats = reinterpret_cast<f32x2 *>(ws + tp.bwd.off_stats);
+  p.stats_stride = tp.bwd.stats_stride;
+  p.O = O;
+  p.rden = reinterpret_cast<const float *>(ws + tp.off_rden);
+  p.wsT = reinterpret_cast<float *>(ws + tp.off_t);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dt == LINATTN_BF16 && causal) return run_saved_backward(p, tp, s);
+  // Other types and the non-causal form: the backward after a forward, on
+  // the records the forward left at the same offsets.
+  if (dt == LINATTN_BF16) return run_backward<__bf16>(p, tp.bwd, causal, true, s, dt);
+  return run_backward<float>(p, tp.bwd, causal, true, s, dt);
 }
 
 // Writes S_out/z_out = S0/z0 (or zero) for every head: the N == 0 case of
@@ -531,6 +647,34 @@ linattn_status linattn_backward_after_forward(const void *Q, const void *K, cons
   try {
     return backward_impl(Q, K, V, dO, dQ, dK, dV, B, H, N, C, M, dt, causal ? 1 : 0, true, workspace,
                          workspace_bytes, stream);
+  } catch (...) {
+    return set_status(LINATTN_ERR_ARG, "internal exception");
+  }
+}
+
+size_t linattn_train_workspace_bytes(int B, int H, int N, int C, int M, linattn_dtype dt, int causal) {
+  if (B <= 0 || H <= 0 || N <= 0 || C != 64 || M != 64 || dtype_bytes(dt) == 0) return 0;
+  const TrainPlan p = plan_train((long long)B * H, N, causal, compute_units(), g_segment_override.load());
+  return p.workspace_bytes == SIZE_MAX ? 0 : p.workspace_bytes;
+}
+
+linattn_status linattn_forward_train(const void *Q, const void *K, const void *V, void *O, int B, int H, int N,
+                                     int C, int M, linattn_dtype dt, int causal, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+  try {
+    return forward_train_impl(Q, K, V, O, B, H, N, C, M, dt, causal ? 1 : 0, workspace, workspace_bytes, stream);
+  } catch (...) {
+    return set_status(LINATTN_ERR_ARG, "internal exception");
+  }
+}
+
+linattn_status linattn_backward_train(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                                      void *dQ, void *dK, void *dV, int B, int H, int N, int C, int M,
+                                      linattn_dtype dt, int causal, void *workspace, size_t workspace_bytes,
+                                      void *stream) {
+  try {
+    return backward_train_impl(Q, K, V, O, dO, dQ, dK, dV, B, H, N, C, M, dt, causal ? 1 : 0, workspace,
+                               workspace_bytes, stream);
   } catch (...) {
     return set_status(LINATTN_ERR_ARG, "internal exception");
   }

@@ -59,6 +59,16 @@ struct BwdParams {
   long long stats_stride;
   int sum_in_walk;    // causal: wsF, wsR hold segment totals; each walk sums
                       // its own prefix (suffix) from them
+  // Saved-forward backward (backward_saved_kernels.hpp).
+  const void *O;      // the forward's output
+  const float *rden;  // [heads][stats_stride] 1/den saved by the forward
+  float *wsT;         // [heads][recT] records: totals at u + 1, then suffixes
+  int recT;
+  int walk_k;         // forward segments per walk segment
+  int walk_segments;  // walk segments per head
+  int rev_segments;   // reverse segments per head (the suffix state's anchors)
+  int rev_chunks;     // chunks per reverse segment
+  int rev_sum_in_walk;  // wsT holds totals (no suffix scan ran)
 };
 
 // Row tiles per chunk of the causal backward walks (32-token chunks): the
@@ -512,6 +522,23 @@ __device__ inline void bwd_r_chunk(State &rs, const Frag<E> qraw[NT][4], const F
   for (int jt = 0; jt < NT; ++jt) {
     f32x4 dk[4] = {zero4(), zero4(), zero4(), zero4()};
     f32x4 dv[4] = {zero4(), zero4(), zero4(), zero4()};
+    auto state_terms = [&]() {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {  // R V^T
+        dk[ct] = mac2<E>(dk[ct], rf[ct][0], rf[ct][1], vf[jt][0], vf[jt][1]);
+        dk[ct] = mac2<E>(dk[ct], rf[ct][2], rf[ct][3], vf[jt][2], vf[jt][3]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {  // R^T phi(K)^T
+        dv[mt] = mac2<E>(dv[mt], ro.sa[0][mt], ro.sa[1][mt], kf[jt][0], kf[jt][1]);
+        dv[mt] = mac2<E>(dv[mt], ro.sa[2][mt], ro.sa[3][mt], kf[jt][2], kf[jt][3]);
+      }
+    };
+    // bf16: the state terms first, so that every accumulator chain runs its
+    // 16x16x32 products before its 16x16x16 ones (device_common.hpp, mac1).
+    // fp32 has one product size and keeps the order that spills least.
+    constexpr bool kStateFirst = std::is_same<E, __bf16>::value;
+    if constexpr (kStateFirst) state_terms();
 #pragma unroll
     for (int it = jt; it < NT; ++it) {
       // Rows i = 16 it + 4 g + r, columns j = 16 jt + n, i >= j:
@@ -536,16 +563,7 @@ __device__ inline void bwd_r_chunk(State &rs, const Frag<E> qraw[NT][4], const F
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) dv[mt] = mac1<E>(dv[mt], gt[it][mt], wf);   // G^T W'
     }
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {  // R V^T
-      dk[ct] = mac2<E>(dk[ct], rf[ct][0], rf[ct][1], vf[jt][0], vf[jt][1]);
-      dk[ct] = mac2<E>(dk[ct], rf[ct][2], rf[ct][3], vf[jt][2], vf[jt][3]);
-    }
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {  // R^T phi(K)^T
-      dv[mt] = mac2<E>(dv[mt], ro.sa[0][mt], ro.sa[1][mt], kf[jt][0], kf[jt][1]);
-      dv[mt] = mac2<E>(dv[mt], ro.sa[2][mt], ro.sa[3][mt], kf[jt][2], kf[jt][3]);
-    }
+    if constexpr (!kStateFirst) state_terms();
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       const f32x4 kv = frag_f32(kraw[jt][ct]);

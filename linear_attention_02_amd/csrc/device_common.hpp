@@ -154,8 +154,13 @@ template <> __device__ inline Frag<float> frag_ones<float>() { return {{1.f, 1.f
 // acc += A * B over a list of 16-wide k slices.
 // bf16: pairs of slices go through one v_mfma_f32_16x16x32_bf16 (a lane's 8
 // operand values are the two slices' 4 each; A and B use the same placement,
-// so the contraction pairs matching k), an odd last slice through
-// v_mfma_f32_16x16x16_bf16.  fp32: four v_mfma_f32_16x16x4_f32 per slice,
+// so the contraction pairs matching k); a single slice goes through the same
+// instruction with a zero slice as its partner, which adds nothing to any
+// sum.  v_mfma_f32_16x16x16_bf16 is not used: on MI355X its results were
+// measured to be read stale (in the last two accumulator registers) by a
+// dependent 16x16x32 product three instructions later, and in a dQ tile read
+// by vector instructions at the distances the compiler allows for the
+// 16x16x32 form.  fp32: four v_mfma_f32_16x16x4_f32 per slice,
 // register r of every lane in instruction r.
 // ---------------------------------------------------------------------------
 __device__ inline f32x4 mma2_bf16(f32x4 acc, const Frag<__bf16> &a0, const Frag<__bf16> &a1,
@@ -166,10 +171,8 @@ __device__ inline f32x4 mma2_bf16(f32x4 acc, const Frag<__bf16> &a0, const Frag<
                                                  0, 0, 0);
 }
 __device__ inline f32x4 mma1_bf16(f32x4 acc, const Frag<__bf16> &a, const Frag<__bf16> &b) {
-  const u32x2 av = a.w;
-  const u32x2 bv = b.w;
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av), __builtin_bit_cast(i16x4, bv), acc,
-                                                   0, 0, 0);
+  const Frag<__bf16> zero = {u32x2{0u, 0u}};
+  return mma2_bf16(acc, a, zero, b, zero);
 }
 __device__ inline f32x4 mma1_f32(f32x4 acc, const Frag<float> &a, const Frag<float> &b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[0], b.v[0], acc, 0, 0, 0);

@@ -60,6 +60,8 @@ struct FwdParams {
   const float *z0;     // [heads][64]
   float *S_out;        // natural order final state, written by the last segment
   float *z_out;
+  float *rden;         // [heads][rden_stride] 1/den per token (saving walk only)
+  long long rden_stride;
 };
 
 // ---------------------------------------------------------------------------
@@ -825,10 +827,13 @@ __device__ inline void state_add_records(State &st, const float *first, int coun
 // ---------------------------------------------------------------------------
 // Causal walk: outputs of one segment, starting from its prefix state.
 // ---------------------------------------------------------------------------
-template <class E, int NT, bool kFull>
+// kSave: also store 1/den_i to rdh[t0 + i] as the walk forms it, for the
+// query row as scaled by phi_q_tile (a reader recovers the row's exponent
+// from q_i with phi_row_scale); lanes g = 0 store each row tile's 16.
+template <class E, int NT, bool kFull, bool kSave = false>
 __device__ inline void causal_chunk(State &st, const Frag<E> qf[NT][4], const Frag<E> kf[NT][4],
                                     const Frag<E> kt[NT][4], const Frag<E> vt[NT][4], int rows, E *Oh, long long t0,
-                                    int n16, int g) {
+                                    int n16, int g, float *rdh = nullptr) {
   StateOperands<E> so;
   state_operands<E>(st, so);  // the state before this chunk (updated at the end)
   const Frag<E> ones = frag_ones<E>();
@@ -868,6 +873,9 @@ __device__ inline void causal_chunk(State &st, const Frag<E> qf[NT][4], const Fr
       dt = mac1<E>(dt, ones, af[it]);
     }
     store_rows<E, kFull>(Oh, t0 + 16 * it, rows - 16 * it, nt, dt, n16, g);
+    if constexpr (kSave) {
+      if (g == 0 && (kFull || 16 * it + n16 < rows)) rdh[t0 + 16 * it + n16] = __builtin_amdgcn_rcpf(dt[0]);
+    }
   }
   state_update<E, NT>(st, kt, vt);
 }
@@ -875,10 +883,10 @@ __device__ inline void causal_chunk(State &st, const Frag<E> qf[NT][4], const Fr
 // bf16 chunk body: registers from the slot, refill the slot with the next
 // chunk, then compute.  kFull: every row of the chunk is inside the sequence
 // (all chunks but possibly a segment's last), so no masking is compiled in.
-template <int NT, bool kFull>
+template <int NT, bool kFull, bool kSave = false>
 __device__ inline void causal_chunk_lds(State &st, u32x4 *slot, const __bf16 *const src[3], long long t0,
                                         long long t_end, int rows, __bf16 *Oh, int lane, int n16, int g,
-                                        const Frag<__bf16> &ident) {
+                                        const Frag<__bf16> &ident, float *rdh = nullptr) {
   typedef __bf16 E;
   constexpr int kT = 16 * NT;
   Frag<E> qf[NT][4], kf[NT][4], kt[NT][4], vt[NT][4];
@@ -908,7 +916,7 @@ __device__ inline void causal_chunk_lds(State &st, u32x4 *slot, const __bf16 *co
     }
   }
   row_to_tok<E, NT>(kf, kt, ident);
-  causal_chunk<E, NT, kFull>(st, qf, kf, kt, vt, rows, Oh, t0, n16, g);
+  causal_chunk<E, NT, kFull, kSave>(st, qf, kf, kt, vt, rows, Oh, t0, n16, g, rdh);
 }
 
 // Row tiles per chunk of the bf16 walk: 4 (64-token chunks, the default) or
@@ -922,7 +930,7 @@ __device__ inline void causal_chunk_lds(State &st, u32x4 *slot, const __bf16 *co
 constexpr int kWalkTilesBf16 = LINATTN_WALK_TILES_BF16;
 static_assert(kWalkTilesBf16 == 2 || kWalkTilesBf16 == 4, "the bf16 walk takes 32- or 64-token chunks");
 
-template <class E>
+template <class E, bool kSave = false>
 __device__ inline void causal_walk(const FwdParams &p) {
   const int worker = blockIdx.x;
   const int h = worker % p.heads;
@@ -958,6 +966,7 @@ __device__ inline void causal_walk(const FwdParams &p) {
     constexpr int kT = 16 * NT;
     __shared__ u32x4 slot[Slot<3, NT>::kVec];
     const __bf16 *src[3] = {Qh, Kh, Vh};
+    float *rdh = kSave ? p.rden + (long long)h * p.rden_stride : nullptr;
     // The first chunk's loads go out before the state's, so that their
     // latencies overlap.
     if (t_begin < t_end) stage_issue<3, NT>(slot, src, t_begin, (int)min<long long>(kT, t_end - t_begin), n16, g);
@@ -965,17 +974,18 @@ __device__ inline void causal_walk(const FwdParams &p) {
     for (long long t0 = t_begin; t0 < t_end; t0 += kT) {
       const int rows = (int)min<long long>(kT, t_end - t0);
       // Outstanding vector-memory operations: this chunk's loads, then the
-      // previous chunk's 2*NT output stores (full chunk).  They retire in
-      // order, so waiting down to 2*NT leaves only stores in flight.
+      // previous chunk's 2*NT output stores (full chunk), and its NT 1/den
+      // stores when saving.  They retire in order, so waiting down to that
+      // count leaves only stores in flight.
       if (t0 == t_begin) {
         wait_vmcnt<0>();
       } else {
-        wait_vmcnt<2 * NT>();
+        wait_vmcnt<2 * NT + (kSave ? NT : 0)>();
       }
       if (rows == kT) {
-        causal_chunk_lds<NT, true>(st, slot, src, t0, t_end, rows, Oh, lane, n16, g, ident);
+        causal_chunk_lds<NT, true, kSave>(st, slot, src, t0, t_end, rows, Oh, lane, n16, g, ident, rdh);
       } else {
-        causal_chunk_lds<NT, false>(st, slot, src, t0, t_end, rows, Oh, lane, n16, g, ident);
+        causal_chunk_lds<NT, false, kSave>(st, slot, src, t0, t_end, rows, Oh, lane, n16, g, ident, rdh);
       }
     }
   } else {
@@ -1029,6 +1039,10 @@ __device__ inline void causal_walk(const FwdParams &p) {
 // chunks it is held to 256 registers, two waves per SIMD.
 __global__ __launch_bounds__(64, kWalkTilesBf16 == 2 ? 2 : 1) void causal_walk_kernel_bf16(FwdParams p) {
   causal_walk<__bf16>(p);
+}
+// The same walk, also saving 1/den per token for the saved-forward backward.
+__global__ __launch_bounds__(64, kWalkTilesBf16 == 2 ? 2 : 1) void causal_walk_save_kernel_bf16(FwdParams p) {
+  causal_walk<__bf16, true>(p);
 }
 __global__ __launch_bounds__(64, 1) void causal_walk_kernel_f32(FwdParams p) { causal_walk<float>(p); }
 template <class E> struct WalkKernel;

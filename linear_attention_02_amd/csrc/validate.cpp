@@ -132,6 +132,41 @@ BwdPlan plan_backward(long long heads, long long N, int causal, int cus, int ove
   return b;
 }
 
+TrainPlan plan_train(long long heads, long long N, int causal, int cus, int override_segments) {
+  TrainPlan t;
+  t.bwd = plan_backward(heads, N, causal, cus, override_segments);
+  if (heads <= 0 || N <= 0) return t;
+  const BwdPlan &b = t.bwd;
+  if (b.workspace_bytes == SIZE_MAX) {
+    t.workspace_bytes = SIZE_MAX;
+    return t;
+  }
+  const long long P = b.fwd.segments;
+  if (cus < 1) cus = 1;
+  const long long per_head = std::max(1LL, ceil_div((long long)kTrainWalkGroupsPerCU * cus, heads));
+  t.walk_k = (int)std::max(1LL, P / per_head);
+  t.walk_segments = (int)ceil_div(P, t.walk_k);
+  if (P == 1 && b.fwd.chunks >= kTrainSplitFrom) {
+    t.rev_chunks = (int)ceil_div(b.fwd.chunks, 2);
+    t.rev_segments = (int)ceil_div(b.fwd.chunks, t.rev_chunks);
+  } else {
+    t.rev_chunks = b.fwd.seg_chunks;
+    t.rev_segments = (int)P;
+  }
+  t.recT = t.rev_segments + 1;
+  size_t rden_bytes = 0, t_bytes = 0;
+  if (!mul3((size_t)heads, (size_t)b.stats_stride, 4, &rden_bytes) ||
+      !mul3((size_t)heads, (size_t)t.recT, kStateBytes, &t_bytes) || rden_bytes > SIZE_MAX / 4 ||
+      t_bytes > SIZE_MAX / 4 || b.workspace_bytes > SIZE_MAX / 4) {
+    t.workspace_bytes = SIZE_MAX;
+    return t;
+  }
+  t.off_rden = align256(b.workspace_bytes);
+  t.off_t = align256(t.off_rden + rden_bytes);
+  t.workspace_bytes = t.off_t + t_bytes;
+  return t;
+}
+
 Check check_backward(const void *Q, const void *K, const void *V, const void *dO, const void *dQ, const void *dK,
                      const void *dV, int B, int H, int N, int C, int M, linattn_dtype dt, const void *workspace,
                      size_t workspace_bytes, size_t workspace_needed) {
@@ -199,6 +234,24 @@ Check check_forward(const void *Q, const void *K, const void *V, const void *O, 
     if (overlaps(bw, bq) || overlaps(bw, bk) || overlaps(bw, bv) || overlaps(bw, bo))
       return fail(LINATTN_ERR_ALIAS, "workspace overlaps Q, K, V or O");
   }
+  return Check();
+}
+
+Check check_backward_train(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                           const void *dQ, const void *dK, const void *dV, int B, int H, int N, int C, int M,
+                           linattn_dtype dt, const void *workspace, size_t workspace_bytes, size_t workspace_needed) {
+  const Check c = check_backward(Q, K, V, dO, dQ, dK, dV, B, H, N, C, M, dt, workspace, workspace_bytes,
+                                 workspace_needed);
+  if (!c.ok()) return c;
+  const size_t bytes = (size_t)B * (size_t)H * (size_t)N * 64 * dtype_bytes(dt);
+  if (bytes == 0) return Check();
+  if (O == nullptr) return fail(LINATTN_ERR_NULL, "O must be non-NULL");
+  if (!aligned16(O)) return fail(LINATTN_ERR_ALIGN, "O must be 16-byte aligned");
+  const Buffer bo{O, bytes, "O"};
+  const Buffer others[] = {{dQ, bytes, "dQ"}, {dK, bytes, "dK"}, {dV, bytes, "dV"},
+                           {workspace, workspace_needed, "workspace"}};
+  for (const Buffer &b : others)
+    if (overlaps(bo, b)) return fail(LINATTN_ERR_ALIAS, std::string("O overlaps ") + b.name);
   return Check();
 }
 

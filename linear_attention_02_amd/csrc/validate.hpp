@@ -67,10 +67,48 @@ struct BwdPlan {
 
 BwdPlan plan_backward(long long heads, long long N, int causal, int cus, int override_segments);
 
+// Launch plan of the forward/backward pair that saves 1/den: the backward
+// plan's layout, then [1/den per token] [suffix records], each region
+// 256-byte aligned.  The saved-forward walk covers walk_k consecutive forward
+// segments per workgroup, so that its segment starts are forward segment
+// starts (where the forward's records give the prefix state).
+constexpr int kTrainWalkGroupsPerCU = 1;
+
+// The suffix state (R, r) of the saved-forward walk is carried by
+// subtraction from an exact suffix sum at each reverse-segment start (an
+// anchor).  The rounding left over at a token is about 2^-24 of the largest
+// sum since its anchor, while the true suffix near the end of a sequence is a
+// few tokens' terms, and 1/den_i falls off like 1/i; so the last reverse
+// segment must not start near the beginning.  Reverse segments are the
+// forward segments, except that a one-segment plan of kTrainSplitFrom chunks
+// or more is split in two.
+constexpr long long kTrainSplitFrom = 4;
+
+struct TrainPlan {
+  BwdPlan bwd;
+  int walk_k = 1;            // forward segments per walk segment
+  int walk_segments = 0;     // walk segments per head
+  int rev_segments = 0;      // reverse segments per head (anchors of the suffix state)
+  int rev_chunks = 0;        // chunks per reverse segment
+  int recT = 0;              // suffix records per head (reverse segments + 1)
+  size_t off_rden = 0;       // byte offset of 1/den (stats_stride floats per head)
+  size_t off_t = 0;          // byte offset of the suffix records
+  size_t workspace_bytes = 0;
+};
+
+TrainPlan plan_train(long long heads, long long N, int causal, int cus, int override_segments);
+
 // Q, K, V, dO inputs and dQ, dK, dV outputs, all [B,H,N,64] in `dt`.
 Check check_backward(const void *Q, const void *K, const void *V, const void *dO, const void *dQ, const void *dK,
                      const void *dV, int B, int H, int N, int C, int M, linattn_dtype dt, const void *workspace,
                      size_t workspace_bytes, size_t workspace_needed);
+
+// check_backward plus the forward output O that linattn_backward_train reads:
+// non-NULL, 16-byte aligned, the size of Q, and disjoint from dQ, dK, dV and
+// the workspace.
+Check check_backward_train(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                           const void *dQ, const void *dK, const void *dV, int B, int H, int N, int C, int M,
+                           linattn_dtype dt, const void *workspace, size_t workspace_bytes, size_t workspace_needed);
 
 Check check_state_args(const float *S0, const float *z0, const float *S_out, const float *z_out, int B, int H,
                        const void *Q, const void *K, const void *V, const void *O, size_t qk_bytes,
