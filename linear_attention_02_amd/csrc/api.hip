@@ -360,7 +360,8 @@ linattn_status run_saved_backward(const BwdParams &base, const TrainPlan &tp, hi
   }
   {
     TimerScope t("bwd_saved_walk_bf16", stream);
-    hipLaunchKernelGGL(bwd_saved_walk_kernel, dim3(heads * (unsigned)tp.walk_segments), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(bwd_saved_walk_kernel, dim3(heads * (unsigned)tp.walk_segments), dim3(64 * kSavedWaves), 0, stream,
+                       p);
   }
   if (launch_error("bwd_saved_walk") != LINATTN_OK) return LINATTN_ERR_HIP;
   return set_status(LINATTN_OK, "");

@@ -103,14 +103,18 @@ __device__ inline u32x4 phi_piece(u32x4 v) {
   return o;
 }
 
-// phi'(x) = min(e^x, 1) from phi(x) itself.
-__device__ inline float phi_prime_of_phi(float f) { return fminf(f, 1.f); }
+// phi'(x) = min(e^x, 1) from phi(x) >= 0 itself, as one clamp to [0, 1].
+__device__ inline float phi_prime_of_phi(float f) { return __builtin_amdgcn_fmed3f(f, 0.f, 1.f); }
 
 // Row tiles per chunk of the saved-forward walk (32-token chunks) and chunks
 // the loader holds in registers ahead of the one being computed.
 constexpr int kSavedTiles = 2;
 constexpr int kLoaderDepth = 3;
-constexpr int kSavedSlotVec = Slot<4, kSavedTiles>::kVec + 8 * kSavedTiles;  // phi(Q), phi(K), V, dO, pairs
+// Slot tensors of the walk: phi(Q), phi(K), V, dO and QSN = -phi(Q) / den
+// (each rounded to bf16 as the saved totals round them), then the pairs.
+constexpr int kPhiQ = 0, kPhiK = 1, kVals = 2, kGrad = 3, kQSN = 4, kSlotTensors = 5;
+constexpr int kSavedPairsVec = Slot<kSlotTensors, kSavedTiles>::kVec;
+constexpr int kSavedSlotVec = kSavedPairsVec + 8 * kSavedTiles;
 static_assert(kSavedTiles == 2, "the chunk bodies pair the two row tiles in their state updates");
 
 // ---------------------------------------------------------------------------
@@ -118,7 +122,10 @@ static_assert(kSavedTiles == 2, "the chunk bodies pair the two row tiles in thei
 //    pairs (1/den_i, b_i) of its tokens (padding tokens up to the chunk end
 //    get zeros) and the record u + 1 of (T_u, t_u), in the State layout.
 //    The forward saved 1/den for each query row as its walk scaled it; the
-//    row's exponent is recovered here from q_i with the same rule.
+//    row's exponent is recovered here from q_i with the same rule.  (Measured
+//    on the long-context workload, splitting a segment over 2 or 4 waves of
+//    one workgroup whose partial sums meet in LDS was slower: 199 and 210 us
+//    against 183 us.)
 // ---------------------------------------------------------------------------
 template <int kPolicy> __device__ inline void bwd_saved_totals(const BwdParams &p) {
   typedef __bf16 E;
@@ -245,12 +252,26 @@ template <int kPolicy> __global__ __launch_bounds__(64, 1) void bwd_saved_totals
 
 // ---------------------------------------------------------------------------
 // 3. The walk.  Workgroup (h, s) covers walk segment s: forward segments
-//    s k .. s k + k - 1 (k = p.walk_k).  Waves: 0 loader, 1 dQ, 2 dK, 3 dV.
+//    s k .. s k + k - 1 (k = p.walk_k).  Eight waves, two per SIMD, two of
+//    each role: loaders, dQ, dK and dV (the kernel maps waves to roles).  A
+//    compute wave owns column half x of its output and of its state (the
+//    other products are recomputed by both halves: the 16 x 16 D or W tiles
+//    are cheap next to the state products); loader x moves half of the
+//    tensors.
 // ---------------------------------------------------------------------------
-// Every wave finishes its LDS accesses of the previous chunk before the
-// barrier; the loader writes a slot only after the barrier that follows the
-// compute waves' last read of it.
-__device__ inline void saved_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+constexpr int kSavedWaves = 8;
+// LDS slots in the ring: a loader fills chunk c + 2 while the compute waves
+// read chunk c + 1 and compute chunk c.
+constexpr int kSavedRing = 3;
+
+// Every wave's LDS accesses issued before the barrier have completed when it
+// passes it (the wait is also visible to the compiler's wait counting).  A
+// loader writes a slot only after the barrier that follows the compute waves'
+// last read of it.
+__device__ inline void saved_barrier() {
+  wait_lgkmcnt0();
+  asm volatile("s_barrier" ::: "memory");
+}
 
 struct SavedSeg {
   long long t_begin, t_end;
@@ -267,62 +288,85 @@ __device__ inline SavedSeg saved_segment(const BwdParams &p, int s) {
   return sg;
 }
 
-// One chunk in the loader's registers: lane l holds 16-byte piece (l & 7) of
-// rows 8 i + (l >> 3) of Q, K, V and dO, and the pairs of tokens
-// 2 (l & 15), 2 (l & 15) + 1.  Every load is issued unconditionally (rows
-// past the end repeat the last row; the compute waves mask them), so the
-// compiler's wait counts see a fixed 4 * 2 NT + 1 loads per chunk and can
-// leave the later chunks in flight.
+// One chunk of loader x's tensors in registers: tensor x (Q or K, phi is
+// applied when it is stored) and tensor x + 2 (V or dO).  Lane l holds
+// 16-byte piece (l & 7) of rows 8 i + (l >> 3); loader 0 also holds the pairs
+// of those rows (for QS), loader 1 the pairs of tokens 2 (l & 15),
+// 2 (l & 15) + 1.  Every load is issued
+// unconditionally (rows past the end repeat the last row; the compute waves
+// mask them), so the compiler's wait counts see a fixed number of loads per
+// chunk and can leave the later chunks in flight.
 struct LoaderChunk {
-  u32x4 v[4][2 * kSavedTiles];
+  u32x4 v[2][2 * kSavedTiles];
   u32x4 pr;
+  f32x2 rowpr[2 * kSavedTiles];
 };
-constexpr int kLoaderLoads = 4 * 2 * kSavedTiles + 1;
 
-__device__ inline void loader_fetch(LoaderChunk &L, const __bf16 *const src[4], const f32x2 *pairs_h, long long t0,
+template <int kHalf>
+__device__ inline void loader_fetch(LoaderChunk &L, const __bf16 *const src[2], const f32x2 *pairs_h, long long t0,
                                     int rows, int lane) {
   const int sub = lane >> 3, piece = lane & 7;
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int i = 0; i < 2 * kSavedTiles; ++i) {
       const int row = min(8 * i + sub, rows - 1);
       L.v[t][i] = reinterpret_cast<const u32x4 *>(src[t] + (t0 + row) * kD)[piece];
     }
   // The pairs array holds every token of the chunk (padding tokens as zeros).
-  L.pr = reinterpret_cast<const u32x4 *>(pairs_h + t0)[lane & 15];
+  if constexpr (kHalf == 0) {
+#pragma unroll
+    for (int i = 0; i < 2 * kSavedTiles; ++i) L.rowpr[i] = pairs_h[t0 + 8 * i + sub];
+  } else {
+    L.pr = reinterpret_cast<const u32x4 *>(pairs_h + t0)[lane & 15];
+  }
 }
 
-// Writes a fetched chunk into a slot in the staging layout (stage_index):
-// phi applied to Q and K.
-__device__ inline void loader_store(const LoaderChunk &L, u32x4 *slot, int lane) {
+// QSN piece: the eight rounded phi(q) of a piece times minus the row's 1/den,
+// rounded once (saved_q_operands with sign -1).
+__device__ inline u32x4 qsn_piece(u32x4 phiq, float rd) {
+  rd = -rd;
+  u32x4 o;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) o[w] = pack_bf16(bf16_lo(phiq[w]) * rd, bf16_hi(phiq[w]) * rd);
+  return o;
+}
+
+// Writes a fetched chunk into a slot in the staging layout (stage_index).
+template <int kHalf> __device__ inline void loader_store(const LoaderChunk &L, u32x4 *slot, int lane) {
   const int sub = lane >> 3, piece = lane & 7;
+  auto at = [&](int tensor, int i) -> u32x4 & { return slot[(tensor * 2 * kSavedTiles + i) * 64 + 8 * sub + (piece ^ sub)]; };
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int i = 0; i < 2 * kSavedTiles; ++i)
-      slot[(t * 2 * kSavedTiles + i) * 64 + 8 * sub + (piece ^ sub)] = t < 2 ? phi_piece(L.v[t][i]) : L.v[t][i];
-  if (lane < 8 * kSavedTiles) slot[Slot<4, kSavedTiles>::kVec + lane] = L.pr;
+  for (int i = 0; i < 2 * kSavedTiles; ++i) {
+    const u32x4 ph = phi_piece(L.v[0][i]);
+    at(kHalf, i) = ph;
+    at(kHalf + 2, i) = L.v[1][i];
+    if constexpr (kHalf == 0) at(kQSN, i) = qsn_piece(ph, L.rowpr[i][0]);
+  }
+  if constexpr (kHalf == 1)
+    if (lane < 8 * kSavedTiles) slot[kSavedPairsVec + lane] = L.pr;
 }
 
+template <int kHalf>
 __device__ inline void saved_loader(const BwdParams &p, u32x4 (*ring)[kSavedSlotVec], int h, const SavedSeg &sg,
                                     int lane) {
   constexpr int kT = 16 * kSavedTiles;
   const long long base = (long long)h * p.N * kD;
-  const __bf16 *src[4] = {reinterpret_cast<const __bf16 *>(p.Q) + base, reinterpret_cast<const __bf16 *>(p.K) + base,
-                          reinterpret_cast<const __bf16 *>(p.V) + base, reinterpret_cast<const __bf16 *>(p.dO) + base};
+  const __bf16 *src[2] = {reinterpret_cast<const __bf16 *>(kHalf == 0 ? p.Q : p.K) + base,
+                          reinterpret_cast<const __bf16 *>(kHalf == 0 ? p.V : p.dO) + base};
   const f32x2 *pairs_h = p.stats + (long long)h * p.stats_stride;
   // Chunks past the last one fetch the last one again (unused), keeping
   // every step's loads unconditional.
   auto fetch = [&](LoaderChunk &L, int c) {
     const long long t0 = sg.t_begin + (long long)min(c, sg.chunks - 1) * kT;
-    loader_fetch(L, src, pairs_h, t0, (int)min<long long>(kT, sg.t_end - t0), lane);
+    loader_fetch<kHalf>(L, src, pairs_h, t0, (int)min<long long>(kT, sg.t_end - t0), lane);
   };
-  // Chunk c: write it into slot c & 1 (its previous contents, chunk c - 2,
-  // were last read before the barrier of chunk c - 1), refill the registers
-  // with chunk c + kLoaderDepth, then the barrier that releases chunk c.
+  // Chunk c: write it into slot c mod 3 (its previous contents, chunk c - 3,
+  // were read by the compute waves between the barriers of chunks c - 3 and
+  // c - 1, and this wave has passed the latter), refill the registers with
+  // chunk c + kLoaderDepth, then the barrier that releases chunk c.
   auto step = [&](LoaderChunk &L, int c) {
-    loader_store(L, ring[c & 1], lane);
+    loader_store<kHalf>(L, ring[c % kSavedRing], lane);
     fetch(L, c + kLoaderDepth);
     saved_barrier();
   };
@@ -343,14 +387,119 @@ __device__ inline void saved_loader(const BwdParams &p, u32x4 (*ring)[kSavedSlot
   if (c0 + 1 < sg.chunks) step(L1, c0 + 1);
 }
 
-// Lane (n, g) of a walk wave: 1/den and b of tokens 16 it + 4 g + r (token
-// layout), tokens past the end zero.
+// A compute wave's half of a state.  dQ and dK waves hold transposed tiles
+// [mt][x], tile (mt, ct = 2 hf + x) of S^T or R^T, and z or r of those
+// feature columns; dV waves hold R tiles [ct][x], tile (ct, mt = 2 hf + x).
+struct HalfState {
+  f32x4 S[4][2];
+  f32x4 z[2];
+};
+
+__device__ inline void half_zero(HalfState &st) {
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    st.z[x] = zero4();
+#pragma unroll
+    for (int a = 0; a < 4; ++a) st.S[a][x] = zero4();
+  }
+}
+
+__device__ inline void half_add(HalfState &st, const HalfState &a) {
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    st.z[x] += a.z[x];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) st.S[b][x] += a.S[b][x];
+  }
+}
+
+// Loads half hf of a record: transposed (state_load_record_t, restricted to
+// ct = 2 hf + x) for dQ and dK, or as stored (tiles mt = 2 hf + x, no z) for dV.
+template <bool kTransposed> __device__ inline void half_load_record(HalfState &st, const float *rec, int hf, int lane) {
+  const int n16 = lane & 15, g = lane >> 4;
+  const f32x4 *p = reinterpret_cast<const f32x4 *>(rec);
+  if constexpr (kTransposed) {
+    const int lane_base = 16 * (n16 >> 2) + 4 * g, reg = n16 & 3;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int ct = 2 * hf + x;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st.S[mt][x][r] = rec[((ct * 4 + mt) * 64 + lane_base + r) * 4 + reg];
+      st.z[x] = p[1024 + ct * 4 + g];
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      st.z[x] = zero4();
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) st.S[ct][x] = p[(ct * 4 + 2 * hf + x) * 64 + lane];
+    }
+  }
+}
+
+// st += half hf of a record, element by element (no second state is held).
+template <bool kTransposed> __device__ inline void half_add_record(HalfState &st, const float *rec, int hf, int lane) {
+  const int n16 = lane & 15, g = lane >> 4;
+  const f32x4 *p = reinterpret_cast<const f32x4 *>(rec);
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    if constexpr (kTransposed) {
+      const int ct = 2 * hf + x, lane_base = 16 * (n16 >> 2) + 4 * g, reg = n16 & 3;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st.S[mt][x][r] += rec[((ct * 4 + mt) * 64 + lane_base + r) * 4 + reg];
+      st.z[x] += p[1024 + ct * 4 + g];
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) st.S[ct][x] += p[(ct * 4 + 2 * hf + x) * 64 + lane];
+    }
+  }
+}
+
+// st = records first, first + stride, ... (count of them, added in that order).
+template <bool kTransposed>
+__device__ inline void half_sum_records(HalfState &st, const float *first, int count, long long stride, int hf,
+                                        int lane) {
+  half_zero(st);
+#pragma unroll 1
+  for (int j = 0; j < count; ++j) half_add_record<kTransposed>(st, first + j * stride, hf, lane);
+}
+
+// Row-layout fragments 2 x, 2 x + 1 of tensor tsr, row tile it.
+template <int NT>
+__device__ inline void lds_row_frag_pair(const u32x4 *slot, int tsr, int it, int x, int lane, Frag<__bf16> f[2]) {
+  const int R = 16 * it + (lane & 15), g = lane >> 4;
+  const u32x4 v = slot[tsr * 2 * NT * 64 + stage_index(R, 4 * x + g)];
+  f[0].w[0] = v[0];
+  f[0].w[1] = v[1];
+  f[1].w[0] = v[2];
+  f[1].w[1] = v[3];
+}
+
+// Stores output column tiles 2 x, 2 x + 1 of 16 rows (columns 32 x .. 32 x +
+// 31): lane (n, g) holds row n, columns 32 x + 8 g .. 32 x + 8 g + 7.
 template <bool kFull>
-__device__ inline void saved_stats_tok(const u32x4 *sreg, int rows, int g, f32x4 rdt[kSavedTiles],
-                                       f32x4 bt[kSavedTiles]) {
+__device__ inline void store_half_tiles(__bf16 *base, long long row0, int rows_left, const f32x4 a[2], int x, int n16,
+                                        int g) {
+  const u32x4 v = {pack_bf16(a[0][0], a[0][1]), pack_bf16(a[0][2], a[0][3]), pack_bf16(a[1][0], a[1][1]),
+                   pack_bf16(a[1][2], a[1][3])};
+  if (kFull || n16 < rows_left)
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(base + (row0 + n16) * kD) + 4 * x + g);
+}
+
+// Lane (n, g) of a walk wave: 1/den and b of tokens 16 it + 4 g + r (token
+// layout) from the two pair vectors stats_tok reads, tokens past the end zero.
+template <bool kFull>
+__device__ inline void saved_stats_tok(const u32x4 lo[kSavedTiles], const u32x4 hi[kSavedTiles], int rows, int g,
+                                       f32x4 rdt[kSavedTiles], f32x4 bt[kSavedTiles]) {
 #pragma unroll
   for (int it = 0; it < kSavedTiles; ++it) {
-    stats_tok(sreg, it, g, rdt[it], bt[it]);
+    const f32x4 l = __builtin_bit_cast(f32x4, lo[it]), h = __builtin_bit_cast(f32x4, hi[it]);
+    rdt[it] = f32x4{l[0], l[2], h[0], h[2]};
+    bt[it] = f32x4{l[1], l[3], h[1], h[3]};
     if (!kFull)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -361,316 +510,457 @@ __device__ inline void saved_stats_tok(const u32x4 *sreg, int rows, int g, f32x4
   }
 }
 
-// Slot tensors of the walk.
-constexpr int kPhiQ = 0, kPhiK = 1, kVals = 2, kGrad = 3;
+// Each compute wave splits a chunk's LDS reads in two.  The "early" set, what
+// the chunk's first products need, is read one chunk ahead: after the body
+// of chunk c has started its first products, it issues the early reads of
+// chunk c + 1 (published by the barrier at the top of its iteration).  The
+// "late" set is read at the top of chunk c's own iteration and arrives while
+// the first products run.  The ring keeps chunk c's slot intact until every
+// wave has finished chunk c (a loader refills it only after the barrier of
+// chunk c + 2).  sched_barrier keeps the compiler from moving the reads of
+// chunk c + 1 ahead of the first products.
+__device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// dQ wave, one chunk: dphi(Q)^T = phi(K)^T D^T + (S G^T) / den + z b^T, then
-// S^T += V^T phi(K), z += column sums of phi(K).
+// dQ wave.  Early: V and dO rows and the pairs by row (the D^T tiles and
+// S G^T).  Late: phi(K) tokens and phi(Q) rows of its features, V tokens.
+struct DqEarly {
+  Frag<__bf16> vf[kSavedTiles][4], gf[kSavedTiles][4];
+  f32x2 sr[kSavedTiles];
+};
+
+__device__ inline void issue_dq_early(DqEarly &E, const u32x4 *slot, int lane) {
+  constexpr int NT = kSavedTiles;
+#pragma unroll
+  for (int it = 0; it < NT; ++it) {
+    lds_row_frags<NT>(slot, kVals, it, lane, E.vf[it]);
+    lds_row_frags<NT>(slot, kGrad, it, lane, E.gf[it]);
+    E.sr[it] = stats_row(slot + kSavedPairsVec, it, lane & 15);
+  }
+}
+
+// dQ wave, one chunk, feature columns ct = 2 hf + x:
+// dphi(Q)^T = phi(K)^T D^T + (S G^T) / den + z b^T, then S^T += V^T phi(K),
+// z += column sums of phi(K).  next: the slot of chunk c + 1, or null.
 template <bool kFull>
-__device__ inline void saved_dq_chunk(State &st, const u32x4 *slot, long long t0, int rows, __bf16 *dQh, int lane) {
-  typedef __bf16 E;
+__device__ inline void saved_dq_chunk(HalfState &st, const DqEarly &E, DqEarly &En, const u32x4 *slot,
+                                      const u32x4 *next, long long t0, int rows, __bf16 *dQh, int hf, int lane) {
+  typedef __bf16 E16;
   constexpr int NT = kSavedTiles;
   const int n16 = lane & 15, g = lane >> 4;
-  const u32x4 *sreg = slot + Slot<4, NT>::kVec;
-  Frag<E> qphi[NT][4], vf[NT][4], gf[NT][4], kt[NT][4], vt[NT][4];
-  f32x2 sr[NT];
+  Frag<E16> qphi[NT][2], kt[NT][2], vt[NT][4];
 #pragma unroll
   for (int it = 0; it < NT; ++it) {
-    lds_row_frags<NT>(slot, kPhiQ, it, lane, qphi[it]);
-    lds_row_frags<NT>(slot, kVals, it, lane, vf[it]);
-    lds_row_frags<NT>(slot, kGrad, it, lane, gf[it]);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      kt[it][c] = lds_tok_frag<NT>(slot, kPhiK, it, c, lane);
-      vt[it][c] = lds_tok_frag<NT>(slot, kVals, it, c, lane);
-    }
-    sr[it] = stats_row(sreg, it, n16);
+    for (int x = 0; x < 2; ++x) kt[it][x] = lds_tok_frag<NT>(slot, kPhiK, it, 2 * hf + x, lane);
+    lds_row_frag_pair<NT>(slot, kPhiQ, it, hf, lane, qphi[it]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vt[it][c] = lds_tok_frag<NT>(slot, kVals, it, c, lane);
   }
-  if (!kFull) {
-    zero_tokens<E, NT>(kt, rows, g);
-    zero_tokens<E, NT>(vt, rows, g);
-  }
-  Frag<E> sf[4][4];  // S as the A operand (row = feature, k = value column)
+  // First products, from the early set: the D^T tiles and S G^T.
+  Frag<E16> sf[2][4];  // S as the A operand (row = feature, k = value column)
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) sf[ct][mt] = to_frag<E>(st.S[mt][ct]);
+    for (int mt = 0; mt < 4; ++mt) sf[x][mt] = to_frag<E16>(st.S[mt][x]);
+  // D^T (key j, query i) = (v_j . g_i) / den_i + b_i for j <= i; tile
+  // (it, jt) at df[it * (it + 1) / 2 + jt].
+  Frag<E16> df[NT * (NT + 1) / 2];
+  f32x4 sg[NT][2];
 #pragma unroll
   for (int it = 0; it < NT; ++it) {
-    const float rd = sr[it][0], b = sr[it][1];
-    // D^T (key j, query i) = (v_j . g_i) / den_i + b_i for j <= i.
-    Frag<E> df[NT];
+    const float rd = E.sr[it][0], b = E.sr[it][1];
 #pragma unroll
     for (int jt = 0; jt <= it; ++jt) {
       f32x4 d = zero4();
-      d = mac2<E>(d, vf[jt][0], vf[jt][1], gf[it][0], gf[it][1]);
-      d = mac2<E>(d, vf[jt][2], vf[jt][3], gf[it][2], gf[it][3]);
+      d = mac2<E16>(d, E.vf[jt][0], E.vf[jt][1], E.gf[it][0], E.gf[it][1]);
+      d = mac2<E16>(d, E.vf[jt][2], E.vf[jt][3], E.gf[it][2], E.gf[it][3]);
       d = d * rd + b;
       if (jt == it)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (4 * g + r > n16) d[r] = 0.f;
-      df[jt] = to_frag<E>(d);
-    }
-    f32x4 dq[4] = {zero4(), zero4(), zero4(), zero4()};
-    f32x4 sg[4] = {zero4(), zero4(), zero4(), zero4()};
-#pragma unroll
-    for (int jp = 0; 2 * jp + 1 <= it; ++jp)
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) dq[ct] = mac2<E>(dq[ct], kt[2 * jp][ct], kt[2 * jp + 1][ct], df[2 * jp], df[2 * jp + 1]);
-    if ((it & 1) == 0)
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) dq[ct] = mac1<E>(dq[ct], kt[it][ct], df[it]);
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      sg[ct] = mac2<E>(sg[ct], sf[ct][0], sf[ct][1], gf[it][0], gf[it][1]);
-      sg[ct] = mac2<E>(sg[ct], sf[ct][2], sf[ct][3], gf[it][2], gf[it][3]);
+      df[it * (it + 1) / 2 + jt] = to_frag<E16>(d);
     }
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const f32x4 pq = frag_f32(qphi[it][ct]);
+    for (int x = 0; x < 2; ++x) {
+      sg[it][x] = mac2<E16>(zero4(), sf[x][0], sf[x][1], E.gf[it][0], E.gf[it][1]);
+      sg[it][x] = mac2<E16>(sg[it][x], sf[x][2], sf[x][3], E.gf[it][2], E.gf[it][3]);
+    }
+  }
+  sched_fence();
+  if (next) issue_dq_early(En, next, lane);
+  sched_fence();
+  if (!kFull)
+#pragma unroll
+    for (int it = 0; it < NT; ++it) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) mask_tokens(kt[it][x], 16 * it + 4 * g, rows);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mask_tokens(vt[it][c], 16 * it + 4 * g, rows);
+    }
+#pragma unroll
+  for (int it = 0; it < NT; ++it) {
+    const float rd = E.sr[it][0], b = E.sr[it][1];
+    const Frag<E16> *dft = df + it * (it + 1) / 2;
+    f32x4 dq[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      dq[x] = zero4();
+#pragma unroll
+      for (int jp = 0; 2 * jp + 1 <= it; ++jp)
+        dq[x] = mac2<E16>(dq[x], kt[2 * jp][x], kt[2 * jp + 1][x], dft[2 * jp], dft[2 * jp + 1]);
+      if ((it & 1) == 0) dq[x] = mac1<E16>(dq[x], kt[it][x], dft[it]);
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const f32x4 pq = frag_f32(qphi[it][x]);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        dq[ct][r] = (dq[ct][r] + sg[ct][r] * rd + st.z[ct][r] * b) * phi_prime_of_phi(pq[r]);
+        dq[x][r] = (dq[x][r] + sg[it][x][r] * rd + st.z[x][r] * b) * phi_prime_of_phi(pq[r]);
     }
-    store_tiles<E, kFull>(dQh, t0 + 16 * it, rows - 16 * it, dq, n16, g);
+    store_half_tiles<kFull>(dQh, t0 + 16 * it, rows - 16 * it, dq, hf, n16, g);
   }
-  // S^T += V^T phi(K) (tile [mt][ct]), z += phi(K)^T 1.
-  const Frag<E> ones = frag_ones<E>();
+  // S^T += V^T phi(K) (tiles [mt][x]), z += phi(K)^T 1.
+  const Frag<E16> ones = frag_ones<E16>();
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
+  for (int x = 0; x < 2; ++x) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) st.S[mt][ct] = mac2<E>(st.S[mt][ct], vt[0][mt], vt[1][mt], kt[0][ct], kt[1][ct]);
-    st.z[ct] = mac2<E>(st.z[ct], kt[0][ct], kt[1][ct], ones, ones);
+    for (int mt = 0; mt < 4; ++mt) st.S[mt][x] = mac2<E16>(st.S[mt][x], vt[0][mt], vt[1][mt], kt[0][x], kt[1][x]);
+    st.z[x] = mac2<E16>(st.z[x], kt[0][x], kt[1][x], ones, ones);
   }
 }
 
-// dK wave, one chunk: first R^T -= G^T (phi(Q)/den), r -= phi(Q)^T b (the
-// chunk's own terms), then dphi(K)^T = R V^T + r 1^T + phi(Q)^T D.
-template <bool kFull>
-__device__ inline void saved_dk_chunk(State &st, const u32x4 *slot, long long t0, int rows, __bf16 *dKh, int lane) {
-  typedef __bf16 E;
+// dK wave.  Early: dO tokens and -phi(Q)/den tokens of its features (the
+// state update).  Late: phi(Q) tokens and phi(K) rows of its features, V and
+// dO rows, the pairs by token.
+struct DkEarly {
+  Frag<__bf16> gt[kSavedTiles][4], qsn[kSavedTiles][2];
+};
+
+__device__ inline void issue_dk_early(DkEarly &E, const u32x4 *slot, int hf, int lane) {
   constexpr int NT = kSavedTiles;
-  const int n16 = lane & 15, g = lane >> 4;
-  const u32x4 *sreg = slot + Slot<4, NT>::kVec;
-  Frag<E> qphit[NT][4], gf[NT][4], vf[NT][4], kphi[NT][4], gt[NT][4];
-  f32x4 rdt[NT], bt[NT];
 #pragma unroll
   for (int it = 0; it < NT; ++it) {
-    lds_row_frags<NT>(slot, kPhiK, it, lane, kphi[it]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) E.gt[it][c] = lds_tok_frag<NT>(slot, kGrad, it, c, lane);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) E.qsn[it][x] = lds_tok_frag<NT>(slot, kQSN, it, 2 * hf + x, lane);
+  }
+}
+
+// dK wave, one chunk, feature columns ct = 2 hf + x: first R^T -= G^T
+// (phi(Q)/den), r -= phi(Q)^T b (the chunk's own terms), then
+// dphi(K)^T = R V^T + r 1^T + phi(Q)^T D.  The wave holds -r (negation is
+// exact), so that the chunk's b terms are added as stored.
+template <bool kFull>
+__device__ inline void saved_dk_chunk(HalfState &st, DkEarly &E, DkEarly &En, const u32x4 *slot, const u32x4 *next,
+                                      long long t0, int rows, __bf16 *dKh, int hf, int lane) {
+  typedef __bf16 E16;
+  constexpr int NT = kSavedTiles;
+  const int n16 = lane & 15, g = lane >> 4;
+  Frag<E16> qt[NT][2], kphi[NT][2], vf[NT][4], gf[NT][4];
+  u32x4 slo[NT], shi[NT];
+#pragma unroll
+  for (int it = 0; it < NT; ++it) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) qt[it][x] = lds_tok_frag<NT>(slot, kPhiQ, it, 2 * hf + x, lane);
+    slo[it] = slot[kSavedPairsVec + 8 * it + 2 * g];
+    shi[it] = slot[kSavedPairsVec + 8 * it + 2 * g + 1];
     lds_row_frags<NT>(slot, kVals, it, lane, vf[it]);
     lds_row_frags<NT>(slot, kGrad, it, lane, gf[it]);
+    lds_row_frag_pair<NT>(slot, kPhiK, it, hf, lane, kphi[it]);
+  }
+  if (!kFull) zero_tokens<E16, NT>(E.gt, rows, g);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      qphit[it][c] = lds_tok_frag<NT>(slot, kPhiQ, it, c, lane);
-      gt[it][c] = lds_tok_frag<NT>(slot, kGrad, it, c, lane);
-    }
-  }
-  saved_stats_tok<kFull>(sreg, rows, g, rdt, bt);
-  if (!kFull) {
-    zero_rows<E, NT>(gf, rows, n16);
-    zero_tokens<E, NT>(gt, rows, g);
-  }
-  Frag<E> qt[NT][4], qsn[NT][4];
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      st.S[mt][x] = mac2<E16>(st.S[mt][x], E.gt[0][mt], E.gt[1][mt], E.qsn[0][x], E.qsn[1][x]);
+  sched_fence();
+  if (next) issue_dk_early(En, next, hf, lane);
+  sched_fence();
+  f32x4 rdt[NT], bt[NT];
+  saved_stats_tok<kFull>(slo, shi, rows, g, rdt, bt);
+  if (!kFull) zero_rows<E16, NT>(gf, rows, n16);
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+    st.z[x] = mac2<E16>(st.z[x], qt[0][x], qt[1][x], to_frag<E16>(bt[0]), to_frag<E16>(bt[1]));
+  // D (query i = 16 it + 4 g + r, key j = 16 jt + n) = (g_i . v_j) / den_i + b_i
+  // for i >= j, tile (it, jt) at dfr[it * (it + 1) / 2 + jt] (first, so that
+  // dO rows and the pairs are done with before the state products).
+  Frag<E16> dfr[NT * (NT + 1) / 2];
 #pragma unroll
   for (int it = 0; it < NT; ++it)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) saved_q_operands(qphit[it][c], rdt[it], -1.f, qt[it][c], qsn[it][c]);
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) st.S[mt][ct] = mac2<E>(st.S[mt][ct], gt[0][mt], gt[1][mt], qsn[0][ct], qsn[1][ct]);
-    st.z[ct] = mac2<E>(st.z[ct], qt[0][ct], qt[1][ct], to_frag<E>(-bt[0]), to_frag<E>(-bt[1]));
-  }
-  Frag<E> rf[4][4];  // R as the A operand (row = feature, k = value column)
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) rf[ct][mt] = to_frag<E>(st.S[mt][ct]);
-#pragma unroll
-  for (int jt = 0; jt < NT; ++jt) {
-    // R V^T first: each accumulator chain runs its 16x16x32 products before
-    // its 16x16x16 ones (device_common.hpp, mac1).
-    f32x4 dk[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      dk[ct] = mac2<E>(zero4(), rf[ct][0], rf[ct][1], vf[jt][0], vf[jt][1]);
-      dk[ct] = mac2<E>(dk[ct], rf[ct][2], rf[ct][3], vf[jt][2], vf[jt][3]);
-    }
-#pragma unroll
-    for (int it = jt; it < NT; ++it) {
-      // D (query i = 16 it + 4 g + r, key j = 16 jt + n) = (g_i . v_j) / den_i + b_i, i >= j.
+    for (int jt = 0; jt <= it; ++jt) {
       f32x4 d = zero4();
-      d = mac2<E>(d, gf[it][0], gf[it][1], vf[jt][0], vf[jt][1]);
-      d = mac2<E>(d, gf[it][2], gf[it][3], vf[jt][2], vf[jt][3]);
+      d = mac2<E16>(d, gf[it][0], gf[it][1], vf[jt][0], vf[jt][1]);
+      d = mac2<E16>(d, gf[it][2], gf[it][3], vf[jt][2], vf[jt][3]);
       d = d * rdt[it] + bt[it];
       if (it == jt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (4 * g + r < n16) d[r] = 0.f;
-      const Frag<E> dfr = to_frag<E>(d);
+      dfr[it * (it + 1) / 2 + jt] = to_frag<E16>(d);
+    }
+  Frag<E16> rf[2][4];  // R as the A operand (row = feature, k = value column)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) dk[ct] = mac1<E>(dk[ct], qt[it][ct], dfr);
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) rf[x][mt] = to_frag<E16>(st.S[mt][x]);
+#pragma unroll
+  for (int jt = 0; jt < NT; ++jt) {
+    f32x4 dk[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      dk[x] = mac2<E16>(zero4(), rf[x][0], rf[x][1], vf[jt][0], vf[jt][1]);
+      dk[x] = mac2<E16>(dk[x], rf[x][2], rf[x][3], vf[jt][2], vf[jt][3]);
     }
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const f32x4 pk = frag_f32(kphi[jt][ct]);
+    for (int it = jt; it < NT; ++it)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dk[ct][r] = (dk[ct][r] + st.z[ct][r]) * phi_prime_of_phi(pk[r]);
+      for (int x = 0; x < 2; ++x) dk[x] = mac1<E16>(dk[x], qt[it][x], dfr[it * (it + 1) / 2 + jt]);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const f32x4 pk = frag_f32(kphi[jt][x]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dk[x][r] = (dk[x][r] - st.z[x][r]) * phi_prime_of_phi(pk[r]);
     }
-    store_tiles<E, kFull>(dKh, t0 + 16 * jt, rows - 16 * jt, dk, n16, g);
+    store_half_tiles<kFull>(dKh, t0 + 16 * jt, rows - 16 * jt, dk, hf, n16, g);
   }
 }
 
-// dV wave, one chunk: first R -= (phi(Q)/den)^T G, then
-// dV^T = R^T phi(K)^T + G^T W' with W'_ij = phi(q_i) . phi(k_j) / den_i, i >= j.
-template <bool kFull>
-__device__ inline void saved_dv_chunk(State &st, const u32x4 *slot, long long t0, int rows, __bf16 *dVh, int lane) {
-  typedef __bf16 E;
+// dV wave.  Early: -phi(Q)/den tokens and dO tokens of its value columns
+// (the state update).  Late: the pairs by token, phi(Q) and phi(K) rows.
+struct DvEarly {
+  Frag<__bf16> qsn[kSavedTiles][4], gt[kSavedTiles][2];
+};
+
+__device__ inline void issue_dv_early(DvEarly &E, const u32x4 *slot, int hf, int lane) {
   constexpr int NT = kSavedTiles;
-  const int n16 = lane & 15, g = lane >> 4;
-  const u32x4 *sreg = slot + Slot<4, NT>::kVec;
-  Frag<E> qf[NT][4], kf[NT][4], qphit[NT][4], gt[NT][4];
-  f32x4 rdt[NT], bt[NT];
 #pragma unroll
   for (int it = 0; it < NT; ++it) {
-    lds_row_frags<NT>(slot, kPhiQ, it, lane, qf[it]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) E.qsn[it][c] = lds_tok_frag<NT>(slot, kQSN, it, c, lane);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) E.gt[it][x] = lds_tok_frag<NT>(slot, kGrad, it, 2 * hf + x, lane);
+  }
+}
+
+// dV wave, one chunk, value columns mt = 2 hf + x: first R -= (phi(Q)/den)^T
+// G, then dV^T = R^T phi(K)^T + G^T W' with
+// W'_ij = phi(q_i) . phi(k_j) / den_i, i >= j.
+template <bool kFull>
+__device__ inline void saved_dv_chunk(HalfState &st, DvEarly &E, DvEarly &En, const u32x4 *slot, const u32x4 *next,
+                                      long long t0, int rows, __bf16 *dVh, int hf, int lane) {
+  typedef __bf16 E16;
+  constexpr int NT = kSavedTiles;
+  const int n16 = lane & 15, g = lane >> 4;
+  Frag<E16> qf[NT][4], kf[NT][4];
+  u32x4 slo[NT], shi[NT];
+#pragma unroll
+  for (int it = 0; it < NT; ++it) {
+    slo[it] = slot[kSavedPairsVec + 8 * it + 2 * g];
+    shi[it] = slot[kSavedPairsVec + 8 * it + 2 * g + 1];
     lds_row_frags<NT>(slot, kPhiK, it, lane, kf[it]);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      qphit[it][c] = lds_tok_frag<NT>(slot, kPhiQ, it, c, lane);
-      gt[it][c] = lds_tok_frag<NT>(slot, kGrad, it, c, lane);
-    }
+    lds_row_frags<NT>(slot, kPhiQ, it, lane, qf[it]);
   }
-  saved_stats_tok<kFull>(sreg, rows, g, rdt, bt);
-  if (!kFull) {
-    zero_rows<E, NT>(qf, rows, n16);
-    zero_tokens<E, NT>(gt, rows, g);
-  }
-  Frag<E> qsn[NT][4];
+  if (!kFull)
 #pragma unroll
-  for (int it = 0; it < NT; ++it)
+    for (int it = 0; it < NT; ++it)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      Frag<E> qp_unused;
-      saved_q_operands(qphit[it][c], rdt[it], -1.f, qp_unused, qsn[it][c]);
-    }
+      for (int x = 0; x < 2; ++x) mask_tokens(E.gt[it][x], 16 * it + 4 * g, rows);
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) st.S[ct][mt] = mac2<E>(st.S[ct][mt], qsn[0][ct], qsn[1][ct], gt[0][mt], gt[1][mt]);
-  StateOperands<E> ro;  // R^T as the A operand (row = value column, k = feature)
-  state_operands<E>(st, ro);
+    for (int x = 0; x < 2; ++x)
+      st.S[ct][x] = mac2<E16>(st.S[ct][x], E.qsn[0][ct], E.qsn[1][ct], E.gt[0][x], E.gt[1][x]);
+  sched_fence();
+  if (next) issue_dv_early(En, next, hf, lane);
+  sched_fence();
+  f32x4 rdt[NT], bt[NT];
+  saved_stats_tok<kFull>(slo, shi, rows, g, rdt, bt);
+  if (!kFull) zero_rows<E16, NT>(qf, rows, n16);
+  // W' tiles first (phi(Q) rows and the pairs are then done with), tile
+  // (it, jt) at wf[it * (it + 1) / 2 + jt].
+  Frag<E16> wf[NT * (NT + 1) / 2];
 #pragma unroll
-  for (int jt = 0; jt < NT; ++jt) {
-    // R^T phi(K)^T first, as in the dK wave.
-    f32x4 dv[4];
+  for (int it = 0; it < NT; ++it)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      dv[mt] = mac2<E>(zero4(), ro.sa[0][mt], ro.sa[1][mt], kf[jt][0], kf[jt][1]);
-      dv[mt] = mac2<E>(dv[mt], ro.sa[2][mt], ro.sa[3][mt], kf[jt][2], kf[jt][3]);
-    }
-#pragma unroll
-    for (int it = jt; it < NT; ++it) {
+    for (int jt = 0; jt <= it; ++jt) {
       f32x4 w = zero4();
-      w = mac2<E>(w, qf[it][0], qf[it][1], kf[jt][0], kf[jt][1]);
-      w = mac2<E>(w, qf[it][2], qf[it][3], kf[jt][2], kf[jt][3]);
+      w = mac2<E16>(w, qf[it][0], qf[it][1], kf[jt][0], kf[jt][1]);
+      w = mac2<E16>(w, qf[it][2], qf[it][3], kf[jt][2], kf[jt][3]);
       w = w * rdt[it];
       if (it == jt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (4 * g + r < n16) w[r] = 0.f;
-      const Frag<E> wf = to_frag<E>(w);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) dv[mt] = mac1<E>(dv[mt], gt[it][mt], wf);
+      wf[it * (it + 1) / 2 + jt] = to_frag<E16>(w);
     }
-    store_tiles<E, kFull>(dVh, t0 + 16 * jt, rows - 16 * jt, dv, n16, g);
+  Frag<E16> ro[4][2];  // R^T as the A operand (row = value column, k = feature)
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) ro[ct][x] = to_frag<E16>(st.S[ct][x]);
+#pragma unroll
+  for (int jt = 0; jt < NT; ++jt) {
+    f32x4 dv[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      dv[x] = mac2<E16>(zero4(), ro[0][x], ro[1][x], kf[jt][0], kf[jt][1]);
+      dv[x] = mac2<E16>(dv[x], ro[2][x], ro[3][x], kf[jt][2], kf[jt][3]);
+    }
+#pragma unroll
+    for (int it = jt; it < NT; ++it)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) dv[x] = mac1<E16>(dv[x], E.gt[it][x], wf[it * (it + 1) / 2 + jt]);
+    store_half_tiles<kFull>(dVh, t0 + 16 * jt, rows - 16 * jt, dv, hf, n16, g);
   }
 }
 
-// The suffix state (R, r) from the start of reverse segment ur on: record ur
-// after the suffix scan, or the sum of the totals records ur + 1 .. P, last
-// first; transposed tiles for the dK wave.
-__device__ inline void load_suffix(State &st, const BwdParams &p, int h, int ur, bool transposed, int lane, int n16,
-                                   int g) {
+// Half hf of the suffix state (R, -r) from the start of reverse segment ur
+// on: record ur after the suffix scan, or the sum of the totals records
+// ur + 1 .. P, last first; r negated (the dK wave's form; the dV wave has no
+// r).
+template <bool kTransposed>
+__device__ inline void load_suffix(HalfState &st, const BwdParams &p, int h, int ur, int hf, int lane) {
+  // The record addressing is derived here from an opaque copy of the lane
+  // index, so the compiler recomputes it on this rare path instead of keeping
+  // it in registers across the chunk loop.
+  asm volatile("" : "+v"(lane));
   const float *recs = p.wsT + (long long)h * p.recT * kStateFloats;
   if (p.rev_sum_in_walk) {
-    const float *last = recs + (long long)p.rev_segments * kStateFloats;
-    const int count = p.rev_segments - ur;
-    state_zero(st);
-    if (transposed) {
-      state_add_records_t(st, last, count, -(long long)kStateFloats, n16, g);
-    } else {
-      state_add_records(st, last, count, -(long long)kStateFloats, lane, g);
-    }
-  } else if (transposed) {
-    state_load_record_t(st, recs + (long long)ur * kStateFloats, n16, g);
+    half_sum_records<kTransposed>(st, recs + (long long)p.rev_segments * kStateFloats, p.rev_segments - ur,
+                                  -(long long)kStateFloats, hf, lane);
   } else {
-    state_load_record(st, recs + (long long)ur * kStateFloats, lane, g);
+    half_load_record<kTransposed>(st, recs + (long long)ur * kStateFloats, hf, lane);
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x) st.z[x] = -st.z[x];
+}
+
+// The compute waves' loop.  With kPrefetch, the barrier at the top of chunk
+// c's iteration publishes chunk c + 1, and chunk(E, En, c, next) computes
+// chunk c from its early set E and reads chunk c + 1's early set into En from
+// slot next (null after the last chunk).  Without, the barrier publishes
+// chunk c itself and its early set is read right after it.  Either way every
+// wave passes the barriers of chunks 0 .. chunks - 1 in order.
+template <class Early, bool kPrefetch, class IssueEarly, class Chunk>
+__device__ inline void walk_chunks(int chunks, const u32x4 (*ring)[kSavedSlotVec], IssueEarly &&issue_early,
+                                   Chunk &&chunk) {
+  if constexpr (kPrefetch) {
+    Early e;
+    saved_barrier();
+    issue_early(e, ring[0]);
+    for (int c = 0; c < chunks; ++c) {
+      const bool more = c + 1 < chunks;
+      if (more) saved_barrier();
+      Early en;
+      chunk(e, en, c, more ? ring[(c + 1) % kSavedRing] : nullptr);
+      e = en;
+    }
+  } else {
+    for (int c = 0; c < chunks; ++c) {
+      Early e;
+      saved_barrier();
+      issue_early(e, ring[c % kSavedRing]);
+      chunk(e, e, c, nullptr);
+    }
   }
 }
 
-__global__ __launch_bounds__(256, 1) void bwd_saved_walk_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * kSavedWaves, 1) void bwd_saved_walk_kernel(BwdParams p) {
   constexpr int NT = kSavedTiles;
   constexpr int kT = 16 * NT;
-  __shared__ u32x4 ring[2][kSavedSlotVec];
+  __shared__ u32x4 ring[kSavedRing][kSavedSlotVec];
   const int worker = blockIdx.x;
   const int h = worker % p.heads;
   const int s = worker / p.heads;
   if (s >= p.walk_segments) return;
   const SavedSeg sg = saved_segment(p, s);
   if (sg.chunks == 0) return;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: kept in scalar registers
   const int lane = threadIdx.x & 63;
-  const int n16 = lane & 15, g = lane >> 4;
-  if (wave == 0) {
-    saved_loader(p, ring, h, sg, lane);
+  // Waves w and w + 4 share a SIMD.  Pairing each loader with a dV wave and
+  // each dQ wave with a dK wave balances the four SIMDs' arithmetic:
+  // w 0, 1 loaders; 2, 3 dQ; 4, 5 dV; 6, 7 dK; hf = w & 1.
+  const int hf = wave & 1;
+  const int role = (0x2310 >> (4 * (wave >> 1))) & 15;
+  if (role == 0) {
+    if (hf == 0) {
+      saved_loader<0>(p, ring, h, sg, lane);
+    } else {
+      saved_loader<1>(p, ring, h, sg, lane);
+    }
     return;
   }
   const long long base = (long long)h * p.N * kD;
-  const int u0 = s * p.walk_k;  // first forward segment of this walk segment
-  State st;
-  if (wave == 1) {
-    // Prefix (S, z) at the segment start, from the forward's records.
-    state_zero(st);
-    if (p.recF > 0) {
-      if (p.sum_in_walk) {
-        state_add_records_t(st, p.wsF + (long long)h * p.recF * kStateFloats, u0, kStateFloats, n16, g);
-      } else {
-        state_load_record_t(st, p.wsF + ((long long)h * p.recF + u0) * kStateFloats, n16, g);
-      }
-    }
-  }
-  // The suffix state starts exact at every reverse-segment start (walk
-  // segments begin at one) and is carried by subtraction in between.
   const long long rev_tokens = (long long)p.rev_chunks * kChunk;
-  if (wave != 1) load_suffix(st, p, h, (int)(sg.t_begin / rev_tokens), wave == 2, lane, n16, g);
-  __bf16 *out = reinterpret_cast<__bf16 *>(wave == 1 ? p.dQ : wave == 2 ? p.dK : p.dV) + base;
-  for (int c = 0; c < sg.chunks; ++c) {
-    saved_barrier();
-    const u32x4 *slot = ring[c & 1];
-    const long long t0 = sg.t_begin + (long long)c * kT;
-    const int rows = (int)min<long long>(kT, sg.t_end - t0);
-    if (wave != 1 && c > 0 && t0 % rev_tokens == 0) load_suffix(st, p, h, (int)(t0 / rev_tokens), wave == 2, lane, n16, g);
-    if (wave == 1) {
-      if (rows == kT) {
-        saved_dq_chunk<true>(st, slot, t0, rows, out, lane);
-      } else {
-        saved_dq_chunk<false>(st, slot, t0, rows, out, lane);
-      }
-    } else if (wave == 2) {
-      if (rows == kT) {
-        saved_dk_chunk<true>(st, slot, t0, rows, out, lane);
-      } else {
-        saved_dk_chunk<false>(st, slot, t0, rows, out, lane);
-      }
+  HalfState st;
+  auto chunk_t0 = [&](int c) { return sg.t_begin + (long long)c * kT; };
+  auto chunk_rows = [&](int c) { return (int)min<long long>(kT, sg.t_end - chunk_t0(c)); };
+  // The suffix state starts exact at every reverse-segment start (walk
+  // segments begin at one) and is carried by subtraction in between: chunk
+  // c is an anchor when its start is a multiple of rev_tokens.  The next
+  // anchor is tracked as a chunk index, so no chunk divides.
+  const int anchor_period = (int)(rev_tokens / kT);
+  int next_anchor = anchor_period - (int)((sg.t_begin / kT) % anchor_period);
+  int next_ur = (int)(sg.t_begin / rev_tokens) + 1;  // reverse segment starting at next_anchor
+  auto anchor = [&](int c) {
+    if (c != next_anchor) return false;
+    next_anchor += anchor_period;
+    return true;
+  };
+  if (role == 1) {
+    // Prefix (S, z) at the segment start, from the forward's records.
+    const int u0 = s * p.walk_k;  // first forward segment of this walk segment
+    if (p.recF == 0) {
+      half_zero(st);
+    } else if (p.sum_in_walk) {
+      half_sum_records<true>(st, p.wsF + (long long)h * p.recF * kStateFloats, u0, kStateFloats, hf, lane);
     } else {
-      if (rows == kT) {
-        saved_dv_chunk<true>(st, slot, t0, rows, out, lane);
-      } else {
-        saved_dv_chunk<false>(st, slot, t0, rows, out, lane);
-      }
+      half_load_record<true>(st, p.wsF + ((long long)h * p.recF + u0) * kStateFloats, hf, lane);
     }
+    __bf16 *out = reinterpret_cast<__bf16 *>(p.dQ) + base;
+    walk_chunks<DqEarly, false>(
+        sg.chunks, ring, [&](DqEarly &E, const u32x4 *slot) { issue_dq_early(E, slot, lane); },
+        [&](DqEarly &E, DqEarly &En, int c, const u32x4 *next) {
+          const u32x4 *slot = ring[c % kSavedRing];
+          if (chunk_rows(c) == kT) {
+            saved_dq_chunk<true>(st, E, En, slot, next, chunk_t0(c), kT, out, hf, lane);
+          } else {
+            saved_dq_chunk<false>(st, E, En, slot, next, chunk_t0(c), chunk_rows(c), out, hf, lane);
+          }
+        });
+  } else if (role == 2) {
+    load_suffix<true>(st, p, h, (int)(sg.t_begin / rev_tokens), hf, lane);
+    __bf16 *out = reinterpret_cast<__bf16 *>(p.dK) + base;
+    walk_chunks<DkEarly, true>(
+        sg.chunks, ring, [&](DkEarly &E, const u32x4 *slot) { issue_dk_early(E, slot, hf, lane); },
+        [&](DkEarly &E, DkEarly &En, int c, const u32x4 *next) {
+          const u32x4 *slot = ring[c % kSavedRing];
+          if (anchor(c)) load_suffix<true>(st, p, h, next_ur++, hf, lane);
+          if (chunk_rows(c) == kT) {
+            saved_dk_chunk<true>(st, E, En, slot, next, chunk_t0(c), kT, out, hf, lane);
+          } else {
+            saved_dk_chunk<false>(st, E, En, slot, next, chunk_t0(c), chunk_rows(c), out, hf, lane);
+          }
+        });
+  } else {
+    load_suffix<false>(st, p, h, (int)(sg.t_begin / rev_tokens), hf, lane);
+    __bf16 *out = reinterpret_cast<__bf16 *>(p.dV) + base;
+    walk_chunks<DvEarly, true>(
+        sg.chunks, ring, [&](DvEarly &E, const u32x4 *slot) { issue_dv_early(E, slot, hf, lane); },
+        [&](DvEarly &E, DvEarly &En, int c, const u32x4 *next) {
+          const u32x4 *slot = ring[c % kSavedRing];
+          if (anchor(c)) load_suffix<false>(st, p, h, next_ur++, hf, lane);
+          if (chunk_rows(c) == kT) {
+            saved_dv_chunk<true>(st, E, En, slot, next, chunk_t0(c), kT, out, hf, lane);
+          } else {
+            saved_dv_chunk<false>(st, E, En, slot, next, chunk_t0(c), chunk_rows(c), out, hf, lane);
+          }
+        });
   }
 }
 
