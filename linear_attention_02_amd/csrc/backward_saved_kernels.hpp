@@ -110,11 +110,17 @@ __device__ inline float phi_prime_of_phi(float f) { return __builtin_amdgcn_fmed
 // the loader holds in registers ahead of the one being computed.
 constexpr int kSavedTiles = 2;
 constexpr int kLoaderDepth = 3;
-// Slot tensors of the walk: phi(Q), phi(K), V, dO and QSN = -phi(Q) / den
-// (each rounded to bf16 as the saved totals round them), then the pairs.
+// Slot of the walk: the tensors phi(Q), phi(K), V, dO and QSN = -phi(Q)/den
+// (each rounded to bf16 as the saved totals round them), the pairs, the
+// chunk's three D tiles in the dK waves' operand layout (written by the dQ
+// waves, 64 lanes x 8 bytes each) and b by token in bf16 (written by loader
+// 1, lane g's 16 bytes holding tokens 4 g .. 4 g + 3 of both row tiles).
 constexpr int kPhiQ = 0, kPhiK = 1, kVals = 2, kGrad = 3, kQSN = 4, kSlotTensors = 5;
 constexpr int kSavedPairsVec = Slot<kSlotTensors, kSavedTiles>::kVec;
-constexpr int kSavedSlotVec = kSavedPairsVec + 8 * kSavedTiles;
+constexpr int kSavedDVec = kSavedPairsVec + 8 * kSavedTiles;
+constexpr int kSavedDTiles = kSavedTiles * (kSavedTiles + 1) / 2;
+constexpr int kSavedBVec = kSavedDVec + 32 * kSavedDTiles;
+constexpr int kSavedSlotVec = kSavedBVec + 4;
 static_assert(kSavedTiles == 2, "the chunk bodies pair the two row tiles in their state updates");
 
 // ---------------------------------------------------------------------------
@@ -218,28 +224,34 @@ template <int kPolicy> __device__ inline void bwd_saved_totals(const BwdParams &
         keep_b = b_row[it];
       }
     pairs_h[t0 + 16 * g + n16] = f32x2{keep_rd, keep_b};
-    // Sums: T += (phi(Q)/den)^T G, t += phi(Q)^T b (token layout operands).
+    // Sums: T += (phi(Q)/den)^T G, t += phi(Q)^T b (token layout operands),
+    // two row tiles per product.
 #pragma unroll
-    for (int it = 0; it < NT; ++it) {
-      f32x4 rdt, bt;
+    for (int ip = 0; ip < NT / 2; ++ip) {
+      Frag<E> bf[2], qp[2][4], qs[2][4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        rdt[r] = __shfl(rd_row[it], 4 * g + r, 64);
-        bt[r] = __shfl(b_row[it], 4 * g + r, 64);
-      }
-      const Frag<E> bf = to_frag<E>(bt);
-      Frag<E> qp[4], qs[4];
+      for (int x = 0; x < 2; ++x) {
+        const int it = 2 * ip + x;
+        f32x4 rdt, bt;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        Frag<E> phiq = qt[it][c];
-        phi_frag<E>(phiq);
-        saved_q_operands(phiq, rdt, 1.f, qp[c], qs[c]);
+        for (int r = 0; r < 4; ++r) {
+          rdt[r] = __shfl(rd_row[it], 4 * g + r, 64);
+          bt[r] = __shfl(b_row[it], 4 * g + r, 64);
+        }
+        bf[x] = to_frag<E>(bt);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          Frag<E> phiq = qt[it][c];
+          phi_frag<E>(phiq);
+          saved_q_operands(phiq, rdt, 1.f, qp[x][c], qs[x][c]);
+        }
       }
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc.S[ct][mt] = mac1<E>(acc.S[ct][mt], qs[ct], gt[it][mt]);
-        acc.z[ct] = mac1<E>(acc.z[ct], qp[ct], bf);
+        for (int mt = 0; mt < 4; ++mt)
+          acc.S[ct][mt] = mac2<E>(acc.S[ct][mt], qs[0][ct], qs[1][ct], gt[2 * ip][mt], gt[2 * ip + 1][mt]);
+        acc.z[ct] = mac2<E>(acc.z[ct], qp[0][ct], qp[1][ct], bf[0], bf[1]);
       }
     }
   }
@@ -343,8 +355,17 @@ template <int kHalf> __device__ inline void loader_store(const LoaderChunk &L, u
     at(kHalf + 2, i) = L.v[1][i];
     if constexpr (kHalf == 0) at(kQSN, i) = qsn_piece(ph, L.rowpr[i][0]);
   }
-  if constexpr (kHalf == 1)
+  if constexpr (kHalf == 1) {
     if (lane < 8 * kSavedTiles) slot[kSavedPairsVec + lane] = L.pr;
+    // b of tokens t = 2 l, 2 l + 1 (lane l < 16) at byte 16 g + 8 it + 2 r
+    // of the b vector, t = 16 it + 4 g + r.
+    if (lane < 16) {
+      const int t = 2 * lane;
+      const f32x4 pr = __builtin_bit_cast(f32x4, L.pr);
+      reinterpret_cast<uint32_t *>(slot + kSavedBVec)[4 * ((t & 15) >> 2) + 2 * (t >> 4) + ((t & 3) >> 1)] =
+          pack_bf16(pr[1], pr[3]);
+    }
+  }
 }
 
 template <int kHalf>
@@ -587,6 +608,16 @@ __device__ inline void saved_dq_chunk(HalfState &st, const DqEarly &E, DqEarly &
       sg[it][x] = mac2<E16>(sg[it][x], sf[x][2], sf[x][3], E.gf[it][2], E.gf[it][3]);
     }
   }
+  // The dK waves' D tiles: D (query 4 g + r, key n) is the transpose of
+  // D^T, taken exactly by a product with the identity (df as the A operand).
+  // Wave hf = 0 writes tiles 0 and 2, wave 1 tile 1.
+  {
+    const Frag<E16> ident = frag_identity<E16>(n16, g);
+    u32x2 *dout = reinterpret_cast<u32x2 *>(const_cast<u32x4 *>(slot) + kSavedDVec);
+#pragma unroll
+    for (int t = 0; t < NT * (NT + 1) / 2; ++t)
+      if ((t & 1) == hf) dout[64 * t + lane] = to_frag<E16>(mac1<E16>(zero4(), df[t], ident)).w;
+  }
   sched_fence();
   if (next) issue_dq_early(En, next, lane);
   sched_fence();
@@ -658,18 +689,21 @@ __device__ inline void saved_dk_chunk(HalfState &st, DkEarly &E, DkEarly &En, co
   typedef __bf16 E16;
   constexpr int NT = kSavedTiles;
   const int n16 = lane & 15, g = lane >> 4;
-  Frag<E16> qt[NT][2], kphi[NT][2], vf[NT][4], gf[NT][4];
-  u32x4 slo[NT], shi[NT];
+  Frag<E16> qt[NT][2], kphi[NT][2], vf[NT][4], dfr[NT * (NT + 1) / 2];
 #pragma unroll
   for (int it = 0; it < NT; ++it) {
 #pragma unroll
     for (int x = 0; x < 2; ++x) qt[it][x] = lds_tok_frag<NT>(slot, kPhiQ, it, 2 * hf + x, lane);
-    slo[it] = slot[kSavedPairsVec + 8 * it + 2 * g];
-    shi[it] = slot[kSavedPairsVec + 8 * it + 2 * g + 1];
     lds_row_frags<NT>(slot, kVals, it, lane, vf[it]);
-    lds_row_frags<NT>(slot, kGrad, it, lane, gf[it]);
     lds_row_frag_pair<NT>(slot, kPhiK, it, hf, lane, kphi[it]);
   }
+  // D (query i = 16 it + 4 g + r, key j = 16 jt + n) = (g_i . v_j) / den_i + b_i
+  // for i >= j, tile (it, jt) at dfr[it * (it + 1) / 2 + jt], from the dQ
+  // waves; b by token.
+#pragma unroll
+  for (int t = 0; t < NT * (NT + 1) / 2; ++t) dfr[t].w = reinterpret_cast<const u32x2 *>(slot + kSavedDVec)[64 * t + lane];
+  const u32x4 bv = slot[kSavedBVec + g];
+  const Frag<E16> bt0 = {u32x2{bv[0], bv[1]}}, bt1 = {u32x2{bv[2], bv[3]}};
   if (!kFull) zero_tokens<E16, NT>(E.gt, rows, g);
 #pragma unroll
   for (int x = 0; x < 2; ++x)
@@ -679,30 +713,9 @@ __device__ inline void saved_dk_chunk(HalfState &st, DkEarly &E, DkEarly &En, co
   sched_fence();
   if (next) issue_dk_early(En, next, hf, lane);
   sched_fence();
-  f32x4 rdt[NT], bt[NT];
-  saved_stats_tok<kFull>(slo, shi, rows, g, rdt, bt);
-  if (!kFull) zero_rows<E16, NT>(gf, rows, n16);
+  static_assert(NT == 2, "the b vector holds two row tiles");
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
-    st.z[x] = mac2<E16>(st.z[x], qt[0][x], qt[1][x], to_frag<E16>(bt[0]), to_frag<E16>(bt[1]));
-  // D (query i = 16 it + 4 g + r, key j = 16 jt + n) = (g_i . v_j) / den_i + b_i
-  // for i >= j, tile (it, jt) at dfr[it * (it + 1) / 2 + jt] (first, so that
-  // dO rows and the pairs are done with before the state products).
-  Frag<E16> dfr[NT * (NT + 1) / 2];
-#pragma unroll
-  for (int it = 0; it < NT; ++it)
-#pragma unroll
-    for (int jt = 0; jt <= it; ++jt) {
-      f32x4 d = zero4();
-      d = mac2<E16>(d, gf[it][0], gf[it][1], vf[jt][0], vf[jt][1]);
-      d = mac2<E16>(d, gf[it][2], gf[it][3], vf[jt][2], vf[jt][3]);
-      d = d * rdt[it] + bt[it];
-      if (it == jt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (4 * g + r < n16) d[r] = 0.f;
-      dfr[it * (it + 1) / 2 + jt] = to_frag<E16>(d);
-    }
+  for (int x = 0; x < 2; ++x) st.z[x] = mac2<E16>(st.z[x], qt[0][x], qt[1][x], bt0, bt1);
   Frag<E16> rf[2][4];  // R as the A operand (row = feature, k = value column)
 #pragma unroll
   for (int x = 0; x < 2; ++x)
