@@ -851,6 +851,11 @@ __device__ inline void load_suffix(HalfState &st, const BwdParams &p, int h, int
   }
 #pragma unroll
   for (int x = 0; x < 2; ++x) st.z[x] = -st.z[x];
+  // The loads land here, on this rare path: otherwise the compiler, not
+  // knowing which path a chunk took, waits for every outstanding memory
+  // operation (the previous chunks' output stores included) before the
+  // state's next use on every chunk.
+  wait_vmcnt<0>();
 }
 
 // The compute waves' loop.  With kPrefetch, the barrier at the top of chunk
@@ -895,11 +900,11 @@ __global__ __launch_bounds__(64 * kSavedWaves, 1) void bwd_saved_walk_kernel(Bwd
   if (sg.chunks == 0) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: kept in scalar registers
   const int lane = threadIdx.x & 63;
-  // Waves w and w + 4 share a SIMD.  Pairing each loader with a dV wave and
-  // each dQ wave with a dK wave balances the four SIMDs' arithmetic:
-  // w 0, 1 loaders; 2, 3 dQ; 4, 5 dV; 6, 7 dK; hf = w & 1.
+  // Waves w and w + 4 share a SIMD.  Pairing each loader with a dK wave and
+  // each dQ wave with a dV wave balances the four SIMDs' arithmetic:
+  // w 0, 1 loaders; 2, 3 dQ; 4, 5 dK; 6, 7 dV; hf = w & 1.
   const int hf = wave & 1;
-  const int role = (0x2310 >> (4 * (wave >> 1))) & 15;
+  const int role = wave >> 1;
   if (role == 0) {
     if (hf == 0) {
       saved_loader<0>(p, ring, h, sg, lane);
@@ -935,6 +940,7 @@ __global__ __launch_bounds__(64 * kSavedWaves, 1) void bwd_saved_walk_kernel(Bwd
     } else {
       half_load_record<true>(st, p.wsF + ((long long)h * p.recF + u0) * kStateFloats, hf, lane);
     }
+    wait_vmcnt<0>();
     __bf16 *out = reinterpret_cast<__bf16 *>(p.dQ) + base;
     walk_chunks<DqEarly, false>(
         sg.chunks, ring, [&](DqEarly &E, const u32x4 *slot) { issue_dq_early(E, slot, lane); },
