@@ -327,6 +327,11 @@ template <class E> __device__ inline void bwd_walk_f(const BwdParams &p) {
     __shared__ u32x4 slot[Slot<4, NT>::kVec];
     const __bf16 *src[4] = {Qh, Kh, Vh, Gh};
     if (t_begin < t_end) stage_issue<4, NT>(slot, src, t_begin, (int)min<long long>(kT, t_end - t_begin), n16, g);
+    // The state's loads (and the first chunk's) land here, before the chunk
+    // loop: left in flight, they would make the compiler wait for every
+    // outstanding memory operation, earlier output stores included, at the
+    // state's first use on every chunk.
+    wait_vmcnt<0>();
     for (long long t0 = t_begin; t0 < t_end; t0 += kT) {
       const int rows = (int)min<long long>(kT, t_end - t0);
       // Outstanding: this chunk's loads, then the previous (full) chunk's
@@ -343,6 +348,11 @@ template <class E> __device__ inline void bwd_walk_f(const BwdParams &p) {
       }
     }
   } else {
+    // The state's loads land here, before the chunk
+    // loop: left in flight, they would make the compiler wait for every
+    // outstanding memory operation, earlier output stores included, at the
+    // state's first use on every chunk.
+    wait_vmcnt<0>();
     for (long long t0 = t_begin; t0 < t_end; t0 += kT) {
       const int rows = (int)min<long long>(kT, t_end - t0);
       Frag<E> qraw[NT][4], kf[NT][4], vf[NT][4], gf[NT][4], vt[NT][4], kt[NT][4];
@@ -675,6 +685,11 @@ template <class E> __device__ inline void bwd_walk_r(const BwdParams &p) {
     const __bf16 *src[4] = {Qh, Kh, Vh, Gh};
     stage_issue<4, NT>(slot, src, last, (int)(t_end - last), n16, g);
     stage_stats<NT>(slot + Slot<4, NT>::kVec, stats_h, last, (int)(t_end - last), lane);
+    // The state's loads (and the first chunk's) land here, before the chunk
+    // loop: left in flight, they would make the compiler wait for every
+    // outstanding memory operation, earlier output stores included, at the
+    // state's first use on every chunk.
+    wait_vmcnt<0>();
     bool prev_full = false;
     for (long long t0 = last; t0 >= t_begin; t0 -= kT) {
       const int rows = (int)min<long long>(kT, t_end - t0);
@@ -696,6 +711,11 @@ template <class E> __device__ inline void bwd_walk_r(const BwdParams &p) {
       prev_full = rows == kT;
     }
   } else {
+    // The state's loads land here, before the chunk
+    // loop: left in flight, they would make the compiler wait for every
+    // outstanding memory operation, earlier output stores included, at the
+    // state's first use on every chunk.
+    wait_vmcnt<0>();
     for (long long t0 = last; t0 >= t_begin; t0 -= kT) {
       const int rows = (int)min<long long>(kT, t_end - t0);
       Frag<E> qraw[NT][4], kf[NT][4], kraw[NT][4], vf[NT][4], gf[NT][4], gt[NT][4];

@@ -873,9 +873,11 @@ __device__ inline void causal_chunk(State &st, const Frag<E> qf[NT][4], const Fr
       dt = mac1<E>(dt, ones, af[it]);
     }
     store_rows<E, kFull>(Oh, t0 + 16 * it, rows - 16 * it, nt, dt, n16, g);
-    if constexpr (kSave) {
-      if (g == 0 && (kFull || 16 * it + n16 < rows)) rdh[t0 + 16 * it + n16] = __builtin_amdgcn_rcpf(dt[0]);
-    }
+    // Every register of dt, in every lane group g, holds the denominator of
+    // row n of this tile: the four groups store the same value (one store
+    // instruction, no branch on g).
+    if constexpr (kSave)
+      if (kFull || 16 * it + n16 < rows) rdh[t0 + 16 * it + n16] = __builtin_amdgcn_rcpf(dt[0]);
   }
   state_update<E, NT>(st, kt, vt);
 }
@@ -959,6 +961,12 @@ __device__ inline void causal_walk(const FwdParams &p) {
     }
     if (p.init == kInitTotals)
       state_add_records(st, p.ws + (long long)h * p.records * kStateFloats, s, kStateFloats, lane, g);
+    // The state's loads land before the chunk loop (the first chunk waits
+    // for everything outstanding anyway).  Left in flight, they would make
+    // the compiler wait for all outstanding memory operations, the previous
+    // chunk's output stores among them, at the state's first use on every
+    // chunk.
+    wait_vmcnt<0>();
   };
 
   if constexpr (std::is_same<E, __bf16>::value) {
