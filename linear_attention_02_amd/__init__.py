@@ -10,13 +10,15 @@ present, calls raise.
     forward(q, k, v, causal=True)               -> o
     forward_state(q, k, v, S0=None, z0=None)    -> (o, S_N, z_N)   causal, carries state
     backward(q, k, v, grad_out, causal=True)    -> (dq, dk, dv)
+    forward_train(q, k, v, causal=True)         -> (o, workspace)  saves what backward_train reads
+    backward_train(q, k, v, o, grad_out, ws)    -> (dq, dk, dv)
     decode_step(S, z, q, k, v)                  -> o               updates S, z in place
     decode_step_strided(S, z, q, k, v)          -> o               q, k, v as strided row views
 
 q, k: [B, H, N, 64]; v: [B, H, N, 64]; float32 or bfloat16, contiguous, CUDA.
 Each call runs on the device of its tensors, on that device's current stream
 unless ``stream`` is given.  ``linear_attention_02_amd.autograd.linear_attention``
-wraps forward and backward as a torch.autograd.Function.
+wraps forward_train and backward_train as a torch.autograd.Function.
 """
 from __future__ import annotations
 
@@ -25,9 +27,10 @@ import os
 import re
 from typing import Optional, Tuple
 
-__all__ = ["forward", "forward_noalloc", "forward_state", "backward", "decode_step", "decode_step_strided", "workspace_bytes",
-           "state_workspace_bytes", "backward_workspace_bytes", "lib", "LinattnError", "timer", "set_segments",
-           "plan_segments", "LIB_PATH", "HEADER_PATH"]
+__all__ = ["forward", "forward_noalloc", "forward_state", "backward", "forward_train", "backward_train",
+           "decode_step", "decode_step_strided", "workspace_bytes", "state_workspace_bytes", "backward_workspace_bytes",
+           "train_workspace_bytes", "lib", "LinattnError", "timer", "set_segments", "plan_segments", "LIB_PATH",
+           "HEADER_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # LINATTN_LIB selects another in-tree build (e.g. the 32-token-chunk walk

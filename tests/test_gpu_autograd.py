@@ -1,6 +1,9 @@
 """The autograd binding (GPU tests): gradients through linear_attention equal
-the library's backward bit for bit, on the scan and in-walk prefix paths, and
-a retained graph can be back-propagated twice."""
+the training pair's (linattn_forward_train, linattn_backward_train) bit for
+bit, on the scan and in-walk prefix paths, and a retained graph can be
+back-propagated twice.  Where the pair falls back to the backward that
+reuses the forward's records (fp32, non-causal), they also equal
+linattn_backward's bit for bit."""
 import pytest
 import torch
 
@@ -31,10 +34,15 @@ def test_autograd_matches_library_backward(segments, causal, dtype):
     o = linear_attention(q, k, v, causal)
     assert torch.equal(o, la.forward(q.detach(), k.detach(), v.detach(), causal=causal))
     (o.float() * w).sum().backward(retain_graph=True)
-    ref = la.backward(q.detach(), k.detach(), v.detach(), w.to(q.dtype), causal=causal)
+    qd, kd, vd = q.detach(), k.detach(), v.detach()
+    o2, ws = la.forward_train(qd, kd, vd, causal=causal)
+    ref = la.backward_train(qd, kd, vd, o2, w.to(q.dtype), ws, causal=causal)
     torch.cuda.synchronize()
     for t, r in zip((q, k, v), ref):
         assert torch.equal(t.grad, r)
+    if not (causal and dtype == "bf16"):
+        for t, r in zip((q, k, v), la.backward(qd, kd, vd, w.to(q.dtype), causal=causal)):
+            assert torch.equal(t.grad, r)
     first = [t.grad.clone() for t in (q, k, v)]
     (o.float() * w).sum().backward()  # second pass through the retained graph accumulates
     torch.cuda.synchronize()
