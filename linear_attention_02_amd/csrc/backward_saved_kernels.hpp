@@ -166,12 +166,10 @@ template <int kPolicy> __device__ inline void bwd_saved_totals(const BwdParams &
   if (t_begin < t_end) issue(t_begin);
   for (long long t0 = t_begin; t0 < t_end; t0 += kChunk) {
     const int rows = chunk_rows(t0, t_end);
-    // Outstanding: this chunk's loads, then the previous chunk's pair store.
-    if (t0 == t_begin) {
-      wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<1>();
-    }
+    // Outstanding: the previous chunk's pair store, then this chunk's loads
+    // (issued after that store: the LDS reads below must wait for the loads,
+    // and a store issued after them would be waited for as well).
+    wait_vmcnt<0>();
     Frag<E> qt[NT][4], gt[NT][4], qr[NT][4], gr[NT][4], orow[NT][4];
     float rd_row[NT];
 #pragma unroll
@@ -187,7 +185,6 @@ template <int kPolicy> __device__ inline void bwd_saved_totals(const BwdParams &
       rd_row[it] = reinterpret_cast<const float *>(rreg)[16 * it + n16];
     }
     wait_lgkmcnt0();
-    if (t0 + kChunk < t_end) issue(t0 + kChunk);
     if (rows < kChunk) zero_tokens<E, NT>(gt, rows, g);
     // Token 16 it + n: its true 1/den (0 past the end) and
     // b = -(g . o) / den; lane (n, g) holds 16 of the token's columns.
@@ -224,6 +221,7 @@ template <int kPolicy> __device__ inline void bwd_saved_totals(const BwdParams &
         keep_b = b_row[it];
       }
     pairs_h[t0 + 16 * g + n16] = f32x2{keep_rd, keep_b};
+    if (t0 + kChunk < t_end) issue(t0 + kChunk);
     // Sums: T += (phi(Q)/den)^T G, t += phi(Q)^T b (token layout operands),
     // two row tiles per product.
 #pragma unroll
@@ -729,10 +727,10 @@ __device__ inline void saved_dk_chunk(HalfState &st, DkEarly &E, DkEarly &En, co
       dk[x] = mac2<E16>(zero4(), rf[x][0], rf[x][1], vf[jt][0], vf[jt][1]);
       dk[x] = mac2<E16>(dk[x], rf[x][2], rf[x][3], vf[jt][2], vf[jt][3]);
     }
+    // Query tiles it >= jt: both in one 32-token product for jt = 0.
 #pragma unroll
-    for (int it = jt; it < NT; ++it)
-#pragma unroll
-      for (int x = 0; x < 2; ++x) dk[x] = mac1<E16>(dk[x], qt[it][x], dfr[it * (it + 1) / 2 + jt]);
+    for (int x = 0; x < 2; ++x)
+      dk[x] = jt == 0 ? mac2<E16>(dk[x], qt[0][x], qt[1][x], dfr[0], dfr[1]) : mac1<E16>(dk[x], qt[1][x], dfr[2]);
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const f32x4 pk = frag_f32(kphi[jt][x]);
@@ -824,10 +822,10 @@ __device__ inline void saved_dv_chunk(HalfState &st, DvEarly &E, DvEarly &En, co
       dv[x] = mac2<E16>(zero4(), ro[0][x], ro[1][x], kf[jt][0], kf[jt][1]);
       dv[x] = mac2<E16>(dv[x], ro[2][x], ro[3][x], kf[jt][2], kf[jt][3]);
     }
+    // Query tiles it >= jt: both in one 32-token product for jt = 0.
 #pragma unroll
-    for (int it = jt; it < NT; ++it)
-#pragma unroll
-      for (int x = 0; x < 2; ++x) dv[x] = mac1<E16>(dv[x], E.gt[it][x], wf[it * (it + 1) / 2 + jt]);
+    for (int x = 0; x < 2; ++x)
+      dv[x] = jt == 0 ? mac2<E16>(dv[x], E.gt[0][x], E.gt[1][x], wf[0], wf[1]) : mac1<E16>(dv[x], E.gt[1][x], wf[2]);
     store_half_tiles<kFull>(dVh, t0 + 16 * jt, rows - 16 * jt, dv, hf, n16, g);
   }
 }
