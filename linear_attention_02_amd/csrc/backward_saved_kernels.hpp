@@ -404,6 +404,7 @@ __device__ inline void saved_loader(const BwdParams &p, u32x4 (*ring)[kSavedSlot
   }
   if (c0 < sg.chunks) step(L0, c0);
   if (c0 + 1 < sg.chunks) step(L1, c0 + 1);
+  saved_barrier();  // closing barrier (walk_chunks)
 }
 
 // A compute wave's half of a state.  dQ and dK waves hold transposed tiles
@@ -861,7 +862,10 @@ __device__ inline void load_suffix(HalfState &st, const BwdParams &p, int h, int
 // chunk c from its early set E and reads chunk c + 1's early set into En from
 // slot next (null after the last chunk).  Without, the barrier publishes
 // chunk c itself and its early set is read right after it.  Either way every
-// wave passes the barriers of chunks 0 .. chunks - 1 in order.
+// wave passes the barriers of chunks 0 .. chunks - 1 in order, then one
+// closing barrier (the loaders too).  The dK waves read chunk c's D tiles,
+// which the dQ waves write while computing chunk c, after the barrier that
+// follows it: that is barrier c + 1, and for the last chunk the closing one.
 template <class Early, bool kPrefetch, class IssueEarly, class Chunk>
 __device__ inline void walk_chunks(int chunks, const u32x4 (*ring)[kSavedSlotVec], IssueEarly &&issue_early,
                                    Chunk &&chunk) {
@@ -870,8 +874,11 @@ __device__ inline void walk_chunks(int chunks, const u32x4 (*ring)[kSavedSlotVec
     saved_barrier();
     issue_early(e, ring[0]);
     for (int c = 0; c < chunks; ++c) {
+      // Barrier c + 1: chunk c + 1 is in its slot, and the dQ waves have
+      // written chunk c's D tiles, which the dK waves read in chunk(c).  The
+      // last chunk's is the closing barrier, which every role passes.
+      saved_barrier();
       const bool more = c + 1 < chunks;
-      if (more) saved_barrier();
       Early en;
       chunk(e, en, c, more ? ring[(c + 1) % kSavedRing] : nullptr);
       e = en;
@@ -883,6 +890,7 @@ __device__ inline void walk_chunks(int chunks, const u32x4 (*ring)[kSavedSlotVec
       issue_early(e, ring[c % kSavedRing]);
       chunk(e, e, c, nullptr);
     }
+    saved_barrier();  // closing: the last chunk's D tiles are written
   }
 }
 

@@ -193,6 +193,28 @@ def test_run_to_run_bitwise_determinism_and_repeatable_backward():
         assert torch.equal(x, y) and torch.equal(x, z)
 
 
+@pytest.mark.parametrize("B,H,N", [(1, 1, 32), (1, 64, 32), (1, 64, 64), (2, 48, 17)])
+def test_short_walk_segments_repeated_with_lds_traffic_between(B, H, N):
+    """Walk segments of one or two 32-token chunks, where a segment's last
+    chunk follows its first at once: the dK waves must read that chunk's D
+    tiles only after the dQ waves wrote them.  Between repeats a forward on
+    other data leaves different LDS contents behind; every repeat must equal
+    the first bit for bit, and the first must meet the oracle's bar."""
+    q, k, v = draw_qkv(B, H, N, 64, 64, "bf16", seed=7900 + N)
+    g = draw_grad_output(B, H, N, 64, "bf16", 7900 + N)
+    check_train(q, k, v, g, True, "bf16", label="short segments")
+    qd, kd, vd, gd = (t.cuda() for t in (q, k, v, g))
+    o, ws = la.forward_train(qd, kd, vd, causal=True)
+    first = la.backward_train(qd, kd, vd, o, gd, ws, causal=True)
+    other = [t.cuda() for t in draw_qkv(4, 8, 3000, 64, 64, "bf16", seed=7999)]
+    for rep in range(12):
+        la.forward(*other, causal=rep % 2 == 0)
+        again = la.backward_train(qd, kd, vd, o, gd, ws, causal=True)
+        torch.cuda.synchronize()
+        for x, y in zip(first, again):
+            assert torch.equal(x, y), f"repeat {rep} differs"
+
+
 @pytest.mark.parametrize("name", ["causal_bf16_b16h8n3072", "causal_bf16_b2h8n131072"])
 def test_named_workload_train_full_size(name):
     w = WORKLOADS[name]
