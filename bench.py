@@ -431,7 +431,9 @@ def backward_record(la, torch, w, steps, warmup):
 def sequence_sweep(la, torch, steps, warmup, B=1, H=8, exps=range(9, 17)):
     """Forward and forward+backward time and peak device memory against N
     (causal, bf16, B=1, H=8, C=M=64): the pages' memory/time sweep over
-    sequence lengths 2^9..2^16, for this library's attention alone."""
+    sequence lengths 2^9..2^16, for this library's attention alone.  The
+    forward+backward is timed twice: linattn_forward + linattn_backward, and
+    the training pair linattn_forward_train + linattn_backward_train."""
     from workloads import draw_grad_output, draw_qkv
     rows = []
     for e in exps:
@@ -460,10 +462,25 @@ def sequence_sweep(la, torch, steps, warmup, B=1, H=8, exps=range(9, 17)):
             fwd()
             la.backward(q, k, v, g, causal=True, dq=dq, dk=dk, dv=dv, workspace=bwd_ws)
 
+        # The training pair (what the autograd node runs): forward_train, then
+        # backward_train on its output and workspace.
+        torch.cuda.synchronize()
+        base_t = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        o_t, ws_t = la.forward_train(q, k, v, causal=True)
+        grads = la.backward_train(q, k, v, o_t, g, ws_t, causal=True)
+        torch.cuda.synchronize()
+        peak_train = torch.cuda.max_memory_allocated() - base_t
+        del grads
+
+        def train():
+            la.forward_train(q, k, v, causal=True, out=o_t, workspace=ws_t)
+            la.backward_train(q, k, v, o_t, g, ws_t, causal=True, dq=dq, dk=dk, dv=dv)
+
         res = {"N": N}
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
-        for key, fn in (("fwd_ms", fwd), ("fwd_bwd_ms", fwd_bwd)):
+        for key, fn in (("fwd_ms", fwd), ("fwd_bwd_ms", fwd_bwd), ("train_pair_ms", train)):
             for _ in range(warmup):
                 fn()
             torch.cuda.synchronize()
@@ -491,13 +508,16 @@ def sequence_sweep(la, torch, steps, warmup, B=1, H=8, exps=range(9, 17)):
             res[key] = start.elapsed_time(end) / steps
             del graph
         res["peak_bytes_fwd_bwd"] = int(peak)
+        res["peak_bytes_train_pair"] = int(peak_train)
         res["input_bytes"] = int(4 * q.numel() * 2)
         rows.append(res)
-        del q, k, v, g, o, dq, dk, dv, fwd_ws, bwd_ws
+        del q, k, v, g, o, dq, dk, dv, fwd_ws, bwd_ws, o_t, ws_t
     return {"shape": f"causal bf16 B={B} H={H} C=M=64", "rows": rows,
             "peak_note": "device memory allocated during one forward + backward call beyond the inputs "
-                         "(O, dQ, dK, dV and both workspaces)",
-            "time_note": "fwd_ms, fwd_bwd_ms: one replay of a HIP graph holding the timed calls, per call "
+                         "(O, dQ, dK, dV and both workspaces); peak_bytes_train_pair: the same for "
+                         "forward_train + backward_train (O, dQ, dK, dV and the train workspace)",
+            "time_note": "fwd_ms, fwd_bwd_ms (forward + backward), train_pair_ms (forward_train + "
+                         "backward_train): one replay of a HIP graph holding the timed calls, per call "
                          "(device time); *_eager: a loop of Python calls"}
 
 
