@@ -215,6 +215,28 @@ def test_short_walk_segments_repeated_with_lds_traffic_between(B, H, N):
             assert torch.equal(x, y), f"repeat {rep} differs"
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gradients_linear_in_grad_output_exactly(dtype, causal):
+    """dQ, dK and dV are linear in dL/dO ("[Paper Review] Transformers are
+    RNNs", §3.5: a_i and b_i are linear in g_i, and every gradient is a sum of
+    products with exactly one of them).  Scaling dL/dO by 4 scales every such
+    product and sum by 4 and commutes with rounding, so both backward paths
+    must return exactly 4 times their gradients."""
+    B, H, N = 2, 3, 64 * 9 + 21
+    q, k, v = (t.cuda() for t in draw_qkv(B, H, N, 64, 64, dtype, seed=8100))
+    g = draw_grad_output(B, H, N, 64, dtype, 8100).cuda()
+    note(f"[train] linearity in dO {dtype} causal={causal}")
+    o, ws = la.forward_train(q, k, v, causal=causal)
+    for run in (lambda gg: la.backward_train(q, k, v, o, gg, ws, causal=causal),
+                lambda gg: la.backward(q, k, v, gg, causal=causal)):
+        one = run(g)
+        four = run(g * 4)
+        torch.cuda.synchronize()
+        for a, b in zip(one, four):
+            assert torch.equal(a * 4, b)
+
+
 @pytest.mark.parametrize("name", ["causal_bf16_b16h8n3072", "causal_bf16_b2h8n131072"])
 def test_named_workload_train_full_size(name):
     w = WORKLOADS[name]
