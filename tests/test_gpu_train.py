@@ -237,6 +237,31 @@ def test_gradients_linear_in_grad_output_exactly(dtype, causal):
             assert torch.equal(a * 4, b)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_dq_of_a_token_depends_only_on_its_own_grad_output(causal):
+    """dphi(q_i) = S_i a_i + b_i z_i ("[Paper Review] Transformers are RNNs",
+    §3.5): of dL/dO it reads row i alone.  Changing dL/dO on a few rows must
+    change dQ on those rows only, bit for bit elsewhere, in both backward
+    paths (a mixed-up token or tile index would leak into other rows)."""
+    B, H, N = 1, 4, 64 * 11 + 5
+    q, k, v = (t.cuda() for t in draw_qkv(B, H, N, 64, 64, "bf16", seed=8200))
+    g = draw_grad_output(B, H, N, 64, "bf16", 8200).cuda()
+    rows = torch.tensor([0, 31, 32, 63, 64, 400, N - 1], device="cuda")
+    g2 = g.clone()
+    g2[:, :, rows] = -g2[:, :, rows] + 0.5
+    note(f"[train] dQ locality causal={causal}")
+    o, ws = la.forward_train(q, k, v, causal=causal)
+    for run in (lambda gg: la.backward_train(q, k, v, o, gg, ws, causal=causal),
+                lambda gg: la.backward(q, k, v, gg, causal=causal)):
+        dq1 = run(g)[0]
+        dq2 = run(g2)[0]
+        torch.cuda.synchronize()
+        keep = torch.ones(N, dtype=torch.bool, device="cuda")
+        keep[rows] = False
+        assert torch.equal(dq1[:, :, keep], dq2[:, :, keep])
+        assert not torch.equal(dq1[:, :, rows], dq2[:, :, rows])
+
+
 @pytest.mark.parametrize("name", ["causal_bf16_b16h8n3072", "causal_bf16_b2h8n131072"])
 def test_named_workload_train_full_size(name):
     w = WORKLOADS[name]
