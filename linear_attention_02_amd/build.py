@@ -35,15 +35,19 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False, extra=None, walk_tiles: int = 0, out: str = None) -> str:
+def build(verbose: bool = False, extra=None, walk_tiles: int = 0, walk_ring: bool = False, out: str = None) -> str:
     """Compiles liblinattn.so (or ``out``).  walk_tiles = 2 builds the bf16
-    causal walk with 32-token chunks instead of 64 (a measurement variant)."""
+    causal walk with 32-token chunks instead of 64 (a measurement variant);
+    walk_ring adds a three-slot LDS ring with two chunks in flight, one wave
+    per SIMD (with walk_tiles = 2)."""
     lib = out or LIB
     tmp = lib + ".tmp"
     obj_dir = os.path.join(HERE, "_build" if not out else "_build_" + os.path.basename(out).replace(".", "_"))
     extra = list(extra or [])
     if walk_tiles:
         extra.append(f"-DLINATTN_WALK_TILES_BF16={int(walk_tiles)}")
+    if walk_ring:
+        extra.append("-DLINATTN_WALK_RING=1")
     os.makedirs(obj_dir, exist_ok=True)
     api_o = os.path.join(obj_dir, "api.o")
     val_o = os.path.join(obj_dir, "validate.o")
@@ -78,6 +82,9 @@ if __name__ == "__main__":
     ap.add_argument("-v", action="store_true")
     ap.add_argument("--walk-tiles", type=int, default=0, choices=(0, 2, 4),
                     help="row tiles per chunk of the bf16 causal walk (2: 32-token chunks; default 4)")
+    ap.add_argument("--walk-ring", action="store_true",
+                    help="with --walk-tiles 2: three-slot ring, two chunks in flight, one wave per SIMD")
     ap.add_argument("--out", default=None, help="output path (default: linear_attention_02_amd/liblinattn.so)")
     args, rest = ap.parse_known_args()
-    build(verbose=args.v, extra=[a for a in rest if a.startswith("-R")], walk_tiles=args.walk_tiles, out=args.out)
+    build(verbose=args.v, extra=[a for a in rest if a.startswith("-R")], walk_tiles=args.walk_tiles,
+          walk_ring=args.walk_ring, out=args.out)

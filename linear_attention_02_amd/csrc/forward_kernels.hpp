@@ -298,6 +298,73 @@ __device__ inline Frag<__bf16> lds_tok_frag(const u32x4 *slot, int tsr, int jt, 
   return f;
 }
 
+// As stage_issue, but every lane takes part in every load: rows at or past
+// `rows` read row rows - 1 again.  A chunk then always costs exactly
+// Slot<kTensors, NT>::kLoads load instructions, so a loop with several
+// chunks in flight can count its outstanding loads exactly.  The slot's
+// positions of rows past the end hold copies the caller masks or never stores.
+template <int kTensors, int NT = 4, int kPolicy = kLoadDefault>
+__device__ inline void stage_issue_counted(u32x4 *slot, const __bf16 *const src[kTensors], long long t0, int rows,
+                                           int n16, int g) {
+  const int lane = 16 * g + n16;
+  const int sub = lane >> 3;
+  const int piece = (lane & 7) ^ sub;
+#pragma unroll
+  for (int tsr = 0; tsr < kTensors; ++tsr) {
+#pragma unroll
+    for (int i = 0; i < 2 * NT; ++i) {
+      const int row = min(8 * i + sub, rows - 1);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4 *>(src[tsr] + (t0 + row) * kD) + piece,
+                                       (lds_void *)(slot + (tsr * 2 * NT + i) * 64), 16, 0, kPolicy);
+    }
+  }
+}
+
+// LDS reads issued from inline assembly, for loops that keep several chunks
+// of LDS-DMA loads, or output stores, in flight.  Before an LDS read that
+// follows LDS-DMA loads, the compiler may wait for every outstanding
+// vector-memory operation (the newest DMA loads and the stores included),
+// which would collapse such a pipeline to one chunk.  These reads are
+// invisible to the compiler's wait counting, so the caller (1) has waited for
+// the DMA loads of the chunk it reads itself, and (2) calls lds_reads_done,
+// then passes every value read this way through after_lds_reads, before any
+// use of it.
+template <int NT = 4>
+__device__ inline Frag<__bf16> lds_tok_frag_untracked(const u32x4 *slot, int tsr, int jt, int mt, int lane) {
+  const int src = lane & 15, g = lane >> 4;
+  const int R = 16 * jt + 4 * g + (src >> 2);
+  const int byte = (tsr * 2 * NT * 64 + stage_index(R, 4 * (mt >> 1) + (src & 3))) * 16 + 8 * (mt & 1);
+  const uint32_t addr = (uint32_t)(size_t)(lds_void *)slot + byte;
+  Frag<__bf16> f;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(f.w) : "v"(addr));
+  return f;
+}
+
+// lds_row_frags for bf16 (raw, no phi), read as lds_tok_frag_untracked is.
+template <int NT = 4>
+__device__ inline void lds_row_frags_untracked(const u32x4 *slot, int tsr, int it, int lane, Frag<__bf16> f[4]) {
+  const int R = 16 * it + (lane & 15), g = lane >> 4;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const uint32_t addr = (uint32_t)(size_t)(lds_void *)slot + 16 * (tsr * 2 * NT * 64 + stage_index(R, 4 * x + g));
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    f[2 * x].w = u32x2{v[0], v[1]};
+    f[2 * x + 1].w = u32x2{v[2], v[3]};
+  }
+}
+
+// Waits for every LDS read of this wave (lgkmcnt(0)).  The memory clobber
+// keeps later LDS-DMA refills of the slot after it.
+__device__ inline void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Makes each of the n fragments depend on the lds_reads_done before it, so
+// that no use of them is scheduled ahead of that wait.
+template <int n> __device__ inline void after_lds_reads(Frag<__bf16> *f) {
+#pragma unroll
+  for (int i = 0; i < n; ++i) asm volatile("" : "+v"(f[i].w));
+}
+
 // Walks the chunks [t_begin, t_end), the first one prefetched here.
 // body(slot, t0, rows) runs on each chunk once its loads have landed: it reads
 // the slot into registers, waits for lgkmcnt(0), issues the next chunk's loads
@@ -921,6 +988,62 @@ __device__ inline void causal_chunk_lds(State &st, u32x4 *slot, const __bf16 *co
   causal_chunk<E, NT, kFull, kSave>(st, qf, kf, kt, vt, rows, Oh, t0, n16, g, rdh);
 }
 
+// Chunk body of the ring walk (LINATTN_WALK_RING): the chunk's slot is read
+// with reads the compiler does not track (its loads have landed), and no
+// refill is issued here.
+template <int NT, bool kFull, bool kSave = false>
+__device__ inline void causal_chunk_ring(State &st, const u32x4 *slot, long long t0, int rows, __bf16 *Oh, int lane,
+                                         int n16, int g, const Frag<__bf16> &ident, float *rdh = nullptr) {
+  typedef __bf16 E;
+  Frag<E> qf[NT][4], kf[NT][4], kt[NT][4], vt[NT][4];
+#pragma unroll
+  for (int it = 0; it < NT; ++it) {
+    lds_row_frags_untracked<NT>(slot, 0, it, lane, qf[it]);
+    lds_row_frags_untracked<NT>(slot, 1, it, lane, kf[it]);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) vt[it][mt] = lds_tok_frag_untracked<NT>(slot, 2, it, mt, lane);
+  }
+  lds_reads_done();
+  after_lds_reads<4 * NT>(&qf[0][0]);
+  after_lds_reads<4 * NT>(&kf[0][0]);
+  after_lds_reads<4 * NT>(&vt[0][0]);
+#pragma unroll
+  for (int it = 0; it < NT; ++it) {
+    phi_q_tile<E>(qf[it]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) phi_frag<E>(kf[it][c]);
+  }
+  if (!kFull) {
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) {
+      if (16 * jt + n16 >= rows)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kf[jt][c] = frag_zero<E>();
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mask_tokens(vt[jt][c], 16 * jt + 4 * g, rows);
+    }
+  }
+  row_to_tok<E, NT>(kf, kt, ident);
+  causal_chunk<E, NT, kFull, kSave>(st, qf, kf, kt, vt, rows, Oh, t0, n16, g, rdh);
+}
+
+// s_waitcnt vmcnt(kLoads * later + kStores * stored) for later, stored in
+// 0..2, known only at run time.
+template <int kLoads, int kStores> __device__ inline void wait_ring(int later, int stored) {
+  static_assert(2 * kLoads + 2 * kStores < 64, "vmcnt range");
+  switch (3 * later + stored) {
+  case 0: wait_vmcnt<0>(); break;
+  case 1: wait_vmcnt<kStores>(); break;
+  case 2: wait_vmcnt<2 * kStores>(); break;
+  case 3: wait_vmcnt<kLoads>(); break;
+  case 4: wait_vmcnt<kLoads + kStores>(); break;
+  case 5: wait_vmcnt<kLoads + 2 * kStores>(); break;
+  case 6: wait_vmcnt<2 * kLoads>(); break;
+  case 7: wait_vmcnt<2 * kLoads + kStores>(); break;
+  default: wait_vmcnt<2 * kLoads + 2 * kStores>(); break;
+  }
+}
+
 // Row tiles per chunk of the bf16 walk: 4 (64-token chunks, the default) or
 // 2 (32-token chunks, built with -DLINATTN_WALK_TILES_BF16=2).  The 32-token
 // walk fits in 256 registers, so two waves share a SIMD; it was measured
@@ -931,6 +1054,15 @@ __device__ inline void causal_chunk_lds(State &st, u32x4 *slot, const __bf16 *co
 #endif
 constexpr int kWalkTilesBf16 = LINATTN_WALK_TILES_BF16;
 static_assert(kWalkTilesBf16 == 2 || kWalkTilesBf16 == 4, "the bf16 walk takes 32- or 64-token chunks");
+// LINATTN_WALK_RING=1 (with 32-token chunks): one wave per SIMD and a ring of
+// three 12 KB slots, so that the next chunk's loads go out at the top of each
+// chunk and two chunks are always in flight.
+#ifndef LINATTN_WALK_RING
+#define LINATTN_WALK_RING 0
+#endif
+constexpr bool kWalkRing = LINATTN_WALK_RING != 0;
+static_assert(!kWalkRing || kWalkTilesBf16 == 2, "the ring walk takes 32-token chunks");
+constexpr int kWalkWavesPerSimd = kWalkTilesBf16 == 2 && !kWalkRing ? 2 : 1;
 
 template <class E, bool kSave = false>
 __device__ inline void causal_walk(const FwdParams &p) {
@@ -969,7 +1101,42 @@ __device__ inline void causal_walk(const FwdParams &p) {
     wait_vmcnt<0>();
   };
 
-  if constexpr (std::is_same<E, __bf16>::value) {
+  if constexpr (std::is_same<E, __bf16>::value && kWalkRing) {
+    constexpr int NT = kWalkTilesBf16;
+    constexpr int kT = 16 * NT;
+    constexpr int kRing = 3;
+    // Per chunk: Slot::kLoads counted loads; per full chunk 2 NT output
+    // stores and, when saving, NT 1/den stores.
+    constexpr int kLoads = Slot<3, NT>::kLoads;
+    constexpr int kStores = 2 * NT + (kSave ? NT : 0);
+    __shared__ u32x4 ring[kRing][Slot<3, NT>::kVec];
+    const __bf16 *src[3] = {Qh, Kh, Vh};
+    float *rdh = kSave ? p.rden + (long long)h * p.rden_stride : nullptr;
+    const int n = (int)((t_end - t_begin + kT - 1) / kT);
+    auto issue = [&](int c) {
+      const long long t0 = t_begin + (long long)c * kT;
+      stage_issue_counted<3, NT>(ring[c % kRing], src, t0, (int)min<long long>(kT, t_end - t0), n16, g);
+    };
+    if (n > 0) issue(0);
+    if (n > 1) issue(1);
+    init_state();  // also waits for chunks 0 and 1
+    for (int c = 0; c < n; ++c) {
+      // Slot (c + 2) % 3 held chunk c - 1, read out (and waited for) in the
+      // previous iteration.
+      if (c + 2 < n) issue(c + 2);
+      // Chunk c's loads were followed by those of the later chunks issued so
+      // far (up to two) and by the stores of the chunks computed since (up to
+      // two, all full); everything retires in order.
+      wait_ring<kLoads, kStores>(min(2, n - 1 - c), min(c, 2));
+      const long long t0 = t_begin + (long long)c * kT;
+      const int rows = (int)min<long long>(kT, t_end - t0);
+      if (rows == kT) {
+        causal_chunk_ring<NT, true, kSave>(st, ring[c % kRing], t0, rows, Oh, lane, n16, g, ident, rdh);
+      } else {
+        causal_chunk_ring<NT, false, kSave>(st, ring[c % kRing], t0, rows, Oh, lane, n16, g, ident, rdh);
+      }
+    }
+  } else if constexpr (std::is_same<E, __bf16>::value) {
     constexpr int NT = kWalkTilesBf16;
     constexpr int kT = 16 * NT;
     __shared__ u32x4 slot[Slot<3, NT>::kVec];
@@ -1045,11 +1212,11 @@ __device__ inline void causal_walk(const FwdParams &p) {
 // One wave per SIMD: the walk keeps the state, one chunk's fragments and the
 // products' accumulators in registers (about 480 of the 512).  With 32-token
 // chunks it is held to 256 registers, two waves per SIMD.
-__global__ __launch_bounds__(64, kWalkTilesBf16 == 2 ? 2 : 1) void causal_walk_kernel_bf16(FwdParams p) {
+__global__ __launch_bounds__(64, kWalkWavesPerSimd) void causal_walk_kernel_bf16(FwdParams p) {
   causal_walk<__bf16>(p);
 }
 // The same walk, also saving 1/den per token for the saved-forward backward.
-__global__ __launch_bounds__(64, kWalkTilesBf16 == 2 ? 2 : 1) void causal_walk_save_kernel_bf16(FwdParams p) {
+__global__ __launch_bounds__(64, kWalkWavesPerSimd) void causal_walk_save_kernel_bf16(FwdParams p) {
   causal_walk<__bf16, true>(p);
 }
 __global__ __launch_bounds__(64, 1) void causal_walk_kernel_f32(FwdParams p) { causal_walk<float>(p); }
