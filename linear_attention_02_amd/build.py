@@ -1,6 +1,6 @@
 """Builds liblinattn.so (HIP, gfx950) in-tree.
 
-    python -m linear_attention_02_amd.build [-v] [--walk-tiles 2 --out PATH]
+    python -m linear_attention_02_amd.build [-v] [--walk-tiles 2 [--walk-ring] --out PATH]
 
 Also builds ``validate_host`` objects with the host compiler only when asked
 (``--host-check``), for sanitizer runs of the argument checks without HIP.
