@@ -6,6 +6,9 @@ the segment plan (the library's own, or a forced count that lands in the
 in-walk prefix, the per-element scan or the grouped scan), and whether the
 forward starts from a carried state.  Each is checked against the fp64
 oracle, forward and backward, on the same bars as the other parity tests.
+Unseeded cases also run the training pair (linattn_forward_train, whose
+output must equal the forward's bit for bit, then linattn_backward_train),
+its gradients on the same bars.
 """
 import random
 
@@ -78,3 +81,11 @@ def test_random_shape_matches_oracle(case):
         err, stats = oracle.parity_error(got.float().cpu().double().numpy(), r, m)
         note(f"[random] case {i} {name} err={err:.3e}")
         assert err <= TOL[dtype], (case, name, err, stats)
+    o_t, ws = la.forward_train(qd, kd, vd, causal=causal)
+    assert torch.equal(o_t, o)
+    grads_t = la.backward_train(qd, kd, vd, o_t, g.cuda(), ws, causal=causal)
+    torch.cuda.synchronize()
+    for name, got, r, m in zip(("dq", "dk", "dv"), grads_t, refs, mags):
+        err, stats = oracle.parity_error(got.float().cpu().double().numpy(), r, m)
+        note(f"[random] case {i} train {name} err={err:.3e}")
+        assert err <= TOL[dtype], (case, "train", name, err, stats)
