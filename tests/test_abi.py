@@ -206,3 +206,66 @@ def test_noalloc_forward_rejects_on_the_host(L):
     assert nf(B=64, H=64, N=64, causal=0) == WORKSPACE
     assert "static scratch" in L.linattn_last_error().decode()
     assert nf(B=0) == OK
+
+
+def _ftrain(L, Q=0x100000, K=0x200000, V=0x300000, O=0x400000, B=1, H=1, N=64, C=64, M=64, dt=1, causal=1, ws=None,
+            wsb=0):
+    return L.linattn_forward_train(Q, K, V, O, B, H, N, C, M, dt, causal, ws, wsb, None)
+
+
+def _btrain(L, Q=0x100000, K=0x200000, V=0x300000, O=0x800000, G=0x400000, dQ=0x500000, dK=0x600000, dV=0x700000,
+            B=1, H=1, N=64, C=64, M=64, dt=1, causal=1, ws=None, wsb=0):
+    return L.linattn_backward_train(Q, K, V, O, G, dQ, dK, dV, B, H, N, C, M, dt, causal, ws, wsb, None)
+
+
+def test_training_pair_rejects_bad_arguments(L):
+    # A workspace of the right size, so that each case fails on its own argument.
+    need = L.linattn_train_workspace_bytes(1, 1, 64, 64, 64, 1, 1)
+    ws = dict(ws=0x900000, wsb=need)
+    assert _ftrain(L, O=None, **ws) == NULL
+    assert _ftrain(L, C=32, **ws) == SHAPE
+    assert _ftrain(L, N=-1, **ws) == SHAPE
+    assert _ftrain(L, dt=7, **ws) == DTYPE
+    assert _ftrain(L, Q=0x100008, **ws) == ALIGN
+    assert _ftrain(L, O=0x300000 + 4096, **ws) == ALIAS  # O inside V (8 KiB tensors)
+    assert _btrain(L, O=None, **ws) == NULL
+    assert _btrain(L, G=None, **ws) == NULL
+    assert _btrain(L, C=32, **ws) == SHAPE
+    assert _btrain(L, dt=7, **ws) == DTYPE
+    assert _btrain(L, O=0x800008, **ws) == ALIGN
+    assert _btrain(L, O=0x500000, **ws) == ALIAS  # O is dQ
+    assert _btrain(L, dV=0x100000 + 4096, **ws) == ALIAS  # dV inside Q
+
+
+def test_training_pair_workspace_rules(L):
+    # bf16 causal: even one chunk needs the saved 1/den and the pairs.
+    need = L.linattn_train_workspace_bytes(1, 1, 64, 64, 64, 1, 1)
+    assert need > 0
+    assert _ftrain(L) == WORKSPACE
+    assert _btrain(L) == WORKSPACE
+    assert _ftrain(L, ws=0x900000, wsb=need - 1) == WORKSPACE
+    assert _btrain(L, ws=0x900000, wsb=need - 1) == WORKSPACE
+    assert _btrain(L, ws=0x600000 + 64, wsb=need) == ALIAS  # workspace inside dK
+    assert _btrain(L, ws=0x900008, wsb=need) == ALIGN
+    # The pair's workspace holds the backward's, plus 1/den per token for bf16 causal calls.
+    for dt in (0, 1):
+        for causal in (0, 1):
+            for B, H, N in ((1, 1, 64), (2, 3, 1000), (1, 8, 1 << 16)):
+                t = L.linattn_train_workspace_bytes(B, H, N, 64, 64, dt, causal)
+                b = L.linattn_backward_workspace_bytes(B, H, N, 64, 64, dt, causal)
+                assert t >= b > 0 or (t >= b and not causal)
+                if dt == 1 and causal:
+                    assert t >= b + B * H * N * 4
+    assert L.linattn_train_workspace_bytes(0, 1, 64, 64, 64, 1, 1) == 0
+    assert L.linattn_train_workspace_bytes(1, 1, 64, 32, 64, 1, 1) == 0
+    assert L.linattn_train_workspace_bytes(1, 1, 64, 64, 64, 7, 1) == 0
+
+
+def test_training_pair_and_after_forward_accept_empty_inputs(L):
+    for B, H, N in ((0, 8, 100), (2, 0, 100), (2, 8, 0)):
+        assert L.linattn_forward_train(None, None, None, None, B, H, N, 64, 64, 1, 1, None, 0, None) == OK
+        assert L.linattn_backward_train(None, None, None, None, None, None, None, None, B, H, N, 64, 64, 1, 1, None,
+                                        0, None) == OK
+        assert L.linattn_backward_after_forward(None, None, None, None, None, None, None, B, H, N, 64, 64, 1, 1,
+                                                None, 0, None) == OK
+    assert L.linattn_last_error().decode() == ""
