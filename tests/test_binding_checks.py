@@ -97,3 +97,42 @@ def test_matching_buffers_reach_the_device_check():
     with pytest.raises(la.LinattnError) as e:
         la.forward(q, k, v, causal=True, out=torch.zeros_like(v))
     assert e.value.status == 8
+
+
+@pytest.mark.parametrize("bad, status", [
+    (torch.zeros(1, 2, 10, 64, dtype=torch.float32), 3),
+    (torch.zeros(1, 2, 9, 64, dtype=torch.bfloat16), 2),
+])
+def test_forward_train_out_must_match_v(bad, status):
+    q, k, v = _qkv()
+    with pytest.raises(la.LinattnError) as e:
+        la.forward_train(q, k, v, causal=True, out=bad)
+    assert e.value.status == status
+
+
+@pytest.mark.parametrize("name, bad, status", [
+    ("o", torch.zeros(1, 2, 10, 64, dtype=torch.float32), 3),   # fp32 o for bf16 inputs
+    ("o", torch.zeros(1, 2, 11, 64, dtype=torch.bfloat16), 2),
+    ("o", None, 1),
+    ("grad_out", torch.zeros(1, 2, 9, 64, dtype=torch.bfloat16), 2),
+    ("dq", torch.zeros(1, 2, 10, 64, dtype=torch.float32), 3),
+    ("dv", torch.zeros(1, 2, 11, 64, dtype=torch.bfloat16), 2),
+    ("workspace", None, 8),                                     # forward_train's workspace is required
+])
+def test_backward_train_buffers_are_checked(name, bad, status):
+    q, k, v = _qkv()
+    nbytes = la.train_workspace_bytes(1, 2, 10, q.dtype, True)
+    args = {"o": torch.zeros_like(v), "grad_out": torch.zeros_like(v),
+            "workspace": torch.zeros(nbytes, dtype=torch.uint8)}
+    args[name] = bad
+    extra = {name: bad} if name in ("dq", "dk", "dv") else {}
+    with pytest.raises(la.LinattnError) as e:
+        la.backward_train(q, k, v, args["o"], args["grad_out"], args["workspace"], causal=True, **extra)
+    assert e.value.status == status
+
+
+def test_training_pair_well_formed_cpu_tensors_reach_the_device_check():
+    q, k, v = _qkv()
+    with pytest.raises(la.LinattnError) as e:
+        la.forward_train(q, k, v, causal=True)
+    assert e.value.status == 8
