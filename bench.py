@@ -98,6 +98,76 @@ def measured_copy_peak(torch) -> dict:
             "what": "torch copy_ of 1 GiB fp32 on the device, read + write bytes"}
 
 
+def stream_probes(torch) -> dict:
+    """Times the streaming probes of libstreamprobes.so (see
+    linear_attention_02_amd/probes/stream_probes.hip) on this GPU: the
+    sustained rate of each access pattern the attention kernels use, in GB/s
+    of bytes read plus written, median of 10 launches after 2 warm-ups."""
+    import ctypes
+    from linear_attention_02_amd import build as hip_build
+    if not os.path.exists(hip_build.PROBES_LIB):
+        raise SystemExit("bench.py --probes: libstreamprobes.so is missing (run __graft_entry__.build())")
+    P = ctypes.CDLL(hip_build.PROBES_LIB)
+    vp, ll, ci = ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int
+    P.probe_read_lds.argtypes = [vp, ll, ci, vp, vp]
+    P.probe_copy.argtypes = [vp, vp, ll, ci, ci, vp]
+    P.probe_write.argtypes = [vp, ll, ci, ci, vp]
+    P.probe_mix31.argtypes = [vp, vp, vp, vp, ll, ci, ci, vp]
+    gib = 1 << 30
+    big = torch.empty(2 * gib, dtype=torch.uint8, device="cuda")
+    big.fill_(1)
+    scratch = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    parts = big.view(4, gib // 2)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed(fn, moved):
+        for _ in range(2):
+            rc = fn()
+            if rc != 0:
+                raise RuntimeError(f"probe failed: {rc}")
+        times = []
+        for _ in range(10):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        ms = sorted(times)[len(times) // 2]
+        return {"GBs": moved / (ms * 1e-3) / 1e9, "bytes": moved, "median_ms": ms}
+
+    res = {
+        "read_lds_default": timed(lambda: P.probe_read_lds(big.data_ptr(), 2 * gib, 0, scratch.data_ptr(), stream),
+                                  2 * gib),
+        "read_lds_nontemporal": timed(lambda: P.probe_read_lds(big.data_ptr(), 2 * gib, 1, scratch.data_ptr(),
+                                                               stream), 2 * gib),
+    }
+    policies = {0: "plain", 1: "nt_loads", 2: "nt_stores", 3: "nt_both"}
+
+    def best(name, launch, moved, write_only=False):
+        """Fastest cache policy and workgroup count of one element probe."""
+        runs = {}
+        for pol in ((0, 2) if write_only else (0, 1, 2, 3)):
+            for blocks in (512, 2048):
+                runs[f"{policies[pol]}_b{blocks}"] = timed(lambda: launch(pol, blocks), moved)
+        key = max(runs, key=lambda k: runs[k]["GBs"])
+        res[name] = dict(runs[key], best_of=key, all_GBs={k: round(v["GBs"]) for k, v in runs.items()})
+
+    best("copy", lambda pol, blocks: P.probe_copy(parts[0].data_ptr(), parts[2].data_ptr(), gib, pol, blocks,
+                                                   stream), 2 * gib)
+    best("write", lambda pol, blocks: P.probe_write(big.data_ptr(), 2 * gib, pol, blocks, stream), 2 * gib,
+         write_only=True)
+    best("mix_3_reads_1_write", lambda pol, blocks: P.probe_mix31(parts[0].data_ptr(), parts[1].data_ptr(),
+                                                                   parts[2].data_ptr(), parts[3].data_ptr(),
+                                                                   gib // 2, pol, blocks, stream), 2 * gib)
+    del big, scratch, parts
+    res["what"] = ("streaming probes on 2 GiB of traffic each: LDS-DMA staged reads (16 KB chunks, two in flight "
+                   "per wave, 1024 waves); and, each workgroup streaming one contiguous range, a 16-byte copy, "
+                   "16-byte writes, and three 16-byte reads per 16-byte write (the causal walk's mix), each the "
+                   "best of plain and non-temporal loads and stores at 512 and 2048 workgroups")
+    return res
+
+
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +186,9 @@ def parse_args():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     ap.add_argument("--segments", type=int, default=0, help="force segments per head (0 = planner)")
+    ap.add_argument("--probes", action="store_true",
+                    help="also time the streaming probes (libstreamprobes.so): the sustained rate of each access "
+                         "pattern the kernels use, measured in the same run")
     return ap.parse_args()
 
 
@@ -678,6 +751,13 @@ def main():
     result["hbm_measured_copy"] = copy_peak
     result["roofline"]["frac_of_measured_copy"] = achieved / copy_peak["GBs"]
     result["forward_call"]["frac_of_measured_copy"] = result["forward_call"]["achieved_GBs"] / copy_peak["GBs"]
+    if args.probes:
+        log("streaming probes")
+        probes = stream_probes(torch)
+        result["stream_probes"] = probes
+        # The walk moves three reads to one write: its rate against the probe
+        # of that mix measured now, on this device.
+        result["roofline"]["frac_of_probe_mix31"] = achieved / probes["mix_3_reads_1_write"]["GBs"]
     if not args.no_noncausal:
         for key, name in (("causal_cifar_shaped", "causal_bf16_b16h8n3072"), ("noncausal", "noncausal_bf16_b8h8n4096")):
             wn = WORKLOADS[name]

@@ -76,6 +76,22 @@ def build_host_check(out_dir: str, sanitize: bool = True) -> str:
     return exe
 
 
+PROBES_SRC = os.path.join(HERE, "probes", "stream_probes.hip")
+PROBES_LIB = os.path.join(HERE, "libstreamprobes.so")
+
+
+def build_probes(verbose: bool = False) -> str:
+    """Compiles libstreamprobes.so, the streaming kernels bench.py --probes
+    times beside the attention kernels (not part of liblinattn.so)."""
+    tmp = PROBES_LIB + ".tmp"
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-shared", PROBES_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, PROBES_LIB)
+    return PROBES_LIB
+
+
 if __name__ == "__main__":
     import argparse
     ap = argparse.ArgumentParser(description="Build liblinattn.so for gfx950 in-tree.")
