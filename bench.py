@@ -113,6 +113,7 @@ def stream_probes(torch) -> dict:
     P.probe_copy.argtypes = [vp, vp, ll, ci, ci, vp]
     P.probe_write.argtypes = [vp, ll, ci, ci, vp]
     P.probe_mix31.argtypes = [vp, vp, vp, vp, ll, ci, ci, vp]
+    P.probe_mix31_lds.argtypes = [vp, vp, vp, vp, ll, ci, vp]
     gib = 1 << 30
     big = torch.empty(2 * gib, dtype=torch.uint8, device="cuda")
     big.fill_(1)
@@ -160,11 +161,16 @@ def stream_probes(torch) -> dict:
     best("mix_3_reads_1_write", lambda pol, blocks: P.probe_mix31(parts[0].data_ptr(), parts[1].data_ptr(),
                                                                    parts[2].data_ptr(), parts[3].data_ptr(),
                                                                    gib // 2, pol, blocks, stream), 2 * gib)
+    res["mix_3_reads_1_write_walk_shaped"] = timed(
+        lambda: P.probe_mix31_lds(parts[0].data_ptr(), parts[1].data_ptr(), parts[2].data_ptr(),
+                                  parts[3].data_ptr(), gib // 2, 1024, stream), 2 * gib)
     del big, scratch, parts
     res["what"] = ("streaming probes on 2 GiB of traffic each: LDS-DMA staged reads (16 KB chunks, two in flight "
                    "per wave, 1024 waves); and, each workgroup streaming one contiguous range, a 16-byte copy, "
                    "16-byte writes, and three 16-byte reads per 16-byte write (the causal walk's mix), each the "
-                   "best of plain and non-temporal loads and stores at 512 and 2048 workgroups")
+                   "best of plain and non-temporal loads and stores at 512 and 2048 workgroups; and the same 3:1 "
+                   "mix in the causal walk's structure (1024 one-wave workgroups, four per CU, one 24 KB chunk "
+                   "of LDS-DMA loads in flight per wave, non-temporal stores, no arithmetic)")
     return res
 
 

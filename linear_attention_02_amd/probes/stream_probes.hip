@@ -12,8 +12,12 @@
 //   probe_write        16-byte stores only.
 //   probe_mix31        three 16-byte reads to one write per element, the
 //                      causal walk's read/write mix (Q, K, V in; O out).
-// The last three take a cache policy (plain or non-temporal loads and
-// stores) and a workgroup count, so that the caller can keep the best.
+//   probe_mix31_lds    the same mix in the causal walk's structure: 64-token
+//                      chunks staged through LDS-DMA, one in flight per
+//                      wave, four waves per CU, no arithmetic.
+// probe_copy, probe_write and probe_mix31 take a cache policy (plain or
+// non-temporal loads and stores) and a workgroup count, so that the caller
+// can keep the best.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -63,6 +67,52 @@ __global__ __launch_bounds__(64) void read_lds_kernel(const u32x4 *src, long lon
     if (c + 2 * kWaves < chunks) issue(c + 2 * kWaves, b);
   }
   if (acc == 0x9e3779b9u) out[blockIdx.x] = acc;  // keeps the reads live
+}
+
+// The causal walk's memory structure without its arithmetic: one wave per
+// workgroup and four per CU (the 40 KB of LDS each takes leaves room for no
+// fifth), each wave streaming a contiguous range of 64-token chunks.  A chunk
+// is 8 KB of each of three inputs, staged through LDS-DMA into one 24 KB
+// slot; the wave waits for it, reads it into registers, issues the next
+// chunk's loads into the same slot, and writes the chunk's 8 KB output (the
+// XOR of the three inputs) with non-temporal stores.  One chunk is in flight
+// per wave while the previous one is written, as in the walk.
+constexpr int kStreamVec = 512;  // 8 KB of one input per chunk
+__global__ __launch_bounds__(64) void mix31_lds_kernel(const u32x4 *a, const u32x4 *b, const u32x4 *c, u32x4 *d,
+                                                       long long chunks) {
+  __shared__ u32x4 slot[2560];  // 24 KB used, 40 KB held
+  const int lane = threadIdx.x;
+  const long long per = (chunks + gridDim.x - 1) / gridDim.x;
+  const long long c0 = (long long)blockIdx.x * per;
+  const long long c1 = c0 + per < chunks ? c0 + per : chunks;
+  auto issue = [&](long long ch) {
+    const u32x4 *src[3] = {a + ch * kStreamVec, b + ch * kStreamVec, c + ch * kStreamVec};
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+#pragma unroll
+      for (int i = 0; i < kStreamVec / 64; ++i)
+        __builtin_amdgcn_global_load_lds(src[s] + i * 64 + lane, (lds_void *)(&slot[s * kStreamVec + i * 64]), 16,
+                                         0, 0);
+  };
+  if (c0 < c1) issue(c0);
+  for (long long ch = c0; ch < c1; ++ch) {
+    wait_vmcnt<0>();  // this chunk has landed (and the previous chunk's stores have gone out)
+    u32x4 x[kStreamVec / 64];
+#pragma unroll
+    for (int i = 0; i < kStreamVec / 64; ++i) {
+      const uint32_t base = (uint32_t)(size_t)(lds_void *)&slot[i * 64 + lane];
+      u32x4 p, q, r;
+      asm volatile("ds_read_b128 %0, %1" : "=v"(p) : "v"(base));
+      asm volatile("ds_read_b128 %0, %1" : "=v"(q) : "v"(base + 16 * kStreamVec));
+      asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(base + 32 * kStreamVec));
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(p), "+v"(q), "+v"(r) : : "memory");
+      x[i] = p ^ q ^ r;
+    }
+    if (ch + 1 < c1) issue(ch + 1);  // the slot has been read
+    u32x4 *out = d + ch * kStreamVec;
+#pragma unroll
+    for (int i = 0; i < kStreamVec / 64; ++i) __builtin_nontemporal_store(x[i], out + i * 64 + lane);
+  }
 }
 
 // The element probes give each workgroup one contiguous range of the
@@ -185,6 +235,20 @@ int probe_write(void *dst, long long bytes, int policy, int blocks, void *stream
     return -1;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   LINATTN_PROBE_POLICY_SWITCH(write_kernel, reinterpret_cast<u32x4 *>(dst), bytes / 16)
+  return (int)hipGetLastError();
+}
+
+// The walk-shaped 3:1 mix: each of a, b, c, d holds `bytes_each`, a
+// multiple of 8 KB; `waves` one-wave workgroups, 1..65536.
+int probe_mix31_lds(const void *a, const void *b, const void *c, void *d, long long bytes_each, int waves,
+                    void *stream) {
+  if (a == nullptr || b == nullptr || c == nullptr || d == nullptr || bytes_each <= 0 ||
+      bytes_each % (16 * kStreamVec) != 0 || waves < 1 || waves > kMaxBlocks)
+    return -1;
+  hipLaunchKernelGGL(mix31_lds_kernel, dim3(waves), dim3(64), 0, reinterpret_cast<hipStream_t>(stream),
+                     reinterpret_cast<const u32x4 *>(a), reinterpret_cast<const u32x4 *>(b),
+                     reinterpret_cast<const u32x4 *>(c), reinterpret_cast<u32x4 *>(d),
+                     bytes_each / (16 * kStreamVec));
   return (int)hipGetLastError();
 }
 
