@@ -1236,16 +1236,45 @@ template <class E> struct ReadSlot;
 template <> struct ReadSlot<__bf16> { static constexpr int kVec = Slot<1>::kVec; };
 template <> struct ReadSlot<float> { static constexpr int kVec = 16 * 4 * 16; };
 
-// tot = sum of the head's `groups` records (16-byte vectors split over the
-// workgroup's threads).
+// tot = sum of the head's `groups` records, added in record order (16-byte
+// vectors split over the workgroup's threads, at most kSumVecs each).  The
+// loads do not depend on the running sums, so each thread issues those of
+// kSumBatch records for all its vectors at once: a record sum costs one load
+// round trip per kSumBatch records rather than one per record and vector.
+constexpr int kSumThreads = 64 * kGroupWaves;
+constexpr int kSumVecs = (kStateVecs + kSumThreads - 1) / kSumThreads;
+constexpr int kSumBatch = 4;
 __device__ inline void sum_group_records(u32x4 *tot, const FwdParams &p, int h, int groups, bool store_total) {
   const f32x4 *recs = reinterpret_cast<const f32x4 *>(p.ws + (long long)h * p.records * kStateFloats);
   f32x4 *total = reinterpret_cast<f32x4 *>(p.ws + ((long long)h * p.records + groups) * kStateFloats);
-  for (int v = threadIdx.x; v < kStateVecs; v += 64 * kGroupWaves) {
-    f32x4 a = recs[v];
-    for (int j = 1; j < groups; ++j) a += recs[(long long)j * kStateVecs + v];
-    tot[v] = __builtin_bit_cast(u32x4, a);
-    if (store_total) total[v] = a;
+  f32x4 acc[kSumVecs];
+#pragma unroll
+  for (int i = 0; i < kSumVecs; ++i) {
+    const int v = threadIdx.x + i * kSumThreads;
+    acc[i] = v < kStateVecs ? recs[v] : zero4();
+  }
+  for (int j0 = 1; j0 < groups; j0 += kSumBatch) {
+    f32x4 r[kSumBatch][kSumVecs];
+#pragma unroll
+    for (int b = 0; b < kSumBatch; ++b)
+#pragma unroll
+      for (int i = 0; i < kSumVecs; ++i) {
+        const int v = threadIdx.x + i * kSumThreads;
+        r[b][i] = j0 + b < groups && v < kStateVecs ? recs[(long long)(j0 + b) * kStateVecs + v] : zero4();
+      }
+#pragma unroll
+    for (int b = 0; b < kSumBatch; ++b)
+      if (j0 + b < groups)
+#pragma unroll
+        for (int i = 0; i < kSumVecs; ++i) acc[i] += r[b][i];
+  }
+#pragma unroll
+  for (int i = 0; i < kSumVecs; ++i) {
+    const int v = threadIdx.x + i * kSumThreads;
+    if (v < kStateVecs) {
+      tot[v] = __builtin_bit_cast(u32x4, acc[i]);
+      if (store_total) total[v] = acc[i];
+    }
   }
 }
 
