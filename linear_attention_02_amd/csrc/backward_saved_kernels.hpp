@@ -46,38 +46,6 @@
 namespace linattn {
 
 // ---------------------------------------------------------------------------
-// Transposed state records.  A record stores S tile (ct, mt) lane (n, g)
-// register r = S[pi(ct,g,r)][pi(mt,n>>2,n&3)] (forward_kernels.hpp).  The
-// transposed tile (mt, ct) holds, in lane (n, g) register r,
-// S[pi(ct,n>>2,n&3)][pi(mt,g,r)]: the record's lane 16 (n>>2) + 4 g + r,
-// register n & 3.  z is loaded as in state_load_record.
-// ---------------------------------------------------------------------------
-__device__ inline void state_load_record_t(State &st, const float *rec, int n16, int g) {
-  const int lane_base = 16 * (n16 >> 2) + 4 * g;
-  const int reg = n16 & 3;
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st.S[mt][ct][r] = rec[((ct * 4 + mt) * 64 + lane_base + r) * 4 + reg];
-  const f32x4 *p = reinterpret_cast<const f32x4 *>(rec);
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) st.z[ct] = p[1024 + ct * 4 + g];
-}
-
-// st += records first, first + stride, ... (count of them, in that order),
-// each loaded transposed.
-__device__ inline void state_add_records_t(State &st, const float *first, int count, long long stride, int n16,
-                                           int g) {
-  for (int j = 0; j < count; ++j) {
-    State a;
-    state_load_record_t(a, first + j * stride, n16, g);
-    state_add(st, a);
-  }
-}
-
-// ---------------------------------------------------------------------------
 // The rounded query operands shared by the saved totals and the walk.  From
 // a token-layout fragment of phi(Q) (already rounded to bf16) and the
 // tokens' 1/den (0 for tokens past the end): qp = phi(q) and
@@ -433,8 +401,12 @@ __device__ inline void half_add(HalfState &st, const HalfState &a) {
   }
 }
 
-// Loads half hf of a record: transposed (state_load_record_t, restricted to
-// ct = 2 hf + x) for dQ and dK, or as stored (tiles mt = 2 hf + x, no z) for dV.
+// Loads half hf of a record.  A record stores S tile (ct, mt) lane (n, g)
+// register r = S[pi(ct,g,r)][pi(mt,n>>2,n&3)] (forward_kernels.hpp).  For dQ
+// and dK it is loaded transposed, tiles (mt, ct) with ct = 2 hf + x: lane
+// (n, g) register r takes S[pi(ct,n>>2,n&3)][pi(mt,g,r)], the record's lane
+// 16 (n>>2) + 4 g + r, register n & 3, and z as state_load_record loads it.
+// For dV it is loaded as stored, tiles mt = 2 hf + x, without z.
 template <bool kTransposed> __device__ inline void half_load_record(HalfState &st, const float *rec, int hf, int lane) {
   const int n16 = lane & 15, g = lane >> 4;
   const f32x4 *p = reinterpret_cast<const f32x4 *>(rec);
