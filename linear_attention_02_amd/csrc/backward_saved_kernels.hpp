@@ -392,15 +392,6 @@ __device__ inline void half_zero(HalfState &st) {
   }
 }
 
-__device__ inline void half_add(HalfState &st, const HalfState &a) {
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    st.z[x] += a.z[x];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) st.S[b][x] += a.S[b][x];
-  }
-}
-
 // Loads half hf of a record.  A record stores S tile (ct, mt) lane (n, g)
 // register r = S[pi(ct,g,r)][pi(mt,n>>2,n&3)] (forward_kernels.hpp).  For dQ
 // and dK it is loaded transposed, tiles (mt, ct) with ct = 2 hf + x: lane
