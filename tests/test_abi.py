@@ -269,3 +269,29 @@ def test_training_pair_and_after_forward_accept_empty_inputs(L):
         assert L.linattn_backward_after_forward(None, None, None, None, None, None, None, B, H, N, 64, 64, 1, 1,
                                                 None, 0, None) == OK
     assert L.linattn_last_error().decode() == ""
+
+
+def test_stream_probe_library_exports_and_host_checks():
+    """libstreamprobes.so (bench.py --probes) loads, exports its probes, and
+    rejects arguments it cannot take before any launch."""
+    from linear_attention_02_amd import build as hip_build
+    assert os.path.exists(hip_build.PROBES_LIB), "libstreamprobes.so not built (run __graft_entry__.build())"
+    P = ctypes.CDLL(hip_build.PROBES_LIB)
+    for n in ("probe_read_lds", "probe_copy", "probe_write", "probe_mix31", "probe_mix31_lds"):
+        assert hasattr(P, n), n
+    vp, ll, ci = ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int
+    P.probe_read_lds.argtypes = [vp, ll, ci, vp, vp]
+    P.probe_copy.argtypes = [vp, vp, ll, ci, ci, vp]
+    P.probe_write.argtypes = [vp, ll, ci, ci, vp]
+    P.probe_mix31.argtypes = [vp, vp, vp, vp, ll, ci, ci, vp]
+    P.probe_mix31_lds.argtypes = [vp, vp, vp, vp, ll, ci, vp]
+    fake = 1 << 20
+    assert P.probe_read_lds(None, 1 << 14, 0, fake, None) == -1
+    assert P.probe_read_lds(fake, (1 << 14) + 16, 0, fake, None) == -1      # not whole 16 KB chunks
+    assert P.probe_copy(fake, fake, 24, 0, 512, None) == -1                 # not whole 16-byte vectors
+    assert P.probe_copy(fake, fake, 1 << 20, 4, 512, None) == -1            # no such policy
+    assert P.probe_write(fake, 1 << 20, 0, 0, None) == -1                   # no workgroups
+    assert P.probe_write(fake, 1 << 20, 0, 65537, None) == -1               # too many workgroups
+    assert P.probe_mix31(fake, None, fake, fake, 1 << 20, 0, 512, None) == -1
+    assert P.probe_mix31_lds(fake, fake, fake, fake, 4096, 1024, None) == -1  # not whole 8 KB chunks
+    assert P.probe_mix31_lds(fake, fake, fake, fake, 1 << 20, 0, None) == -1
