@@ -143,6 +143,11 @@ def stream_probes(torch) -> dict:
         "read_lds_nontemporal": timed(lambda: P.probe_read_lds(big.data_ptr(), 2 * gib, 1, scratch.data_ptr(),
                                                                stream), 2 * gib),
     }
+    # The same reads repeated over buffers that fit the 256 MB last-level cache
+    # (MALL): what a re-read of recently read data can gain.
+    for mib in (128, 256):
+        res[f"read_lds_default_{mib}MiB_repeated"] = timed(
+            lambda: P.probe_read_lds(big.data_ptr(), mib << 20, 0, scratch.data_ptr(), stream), mib << 20)
     policies = {0: "plain", 1: "nt_loads", 2: "nt_stores", 3: "nt_both"}
 
     def best(name, launch, moved, write_only=False):
@@ -166,7 +171,8 @@ def stream_probes(torch) -> dict:
                                   parts[3].data_ptr(), gib // 2, 1024, stream), 2 * gib)
     del big, scratch, parts
     res["what"] = ("streaming probes on 2 GiB of traffic each: LDS-DMA staged reads (16 KB chunks, two in flight "
-                   "per wave, 1024 waves); and, each workgroup streaming one contiguous range, a 16-byte copy, "
+                   "per wave, 1024 waves), also repeated over 128 and 256 MiB buffers that the last-level cache can "
+                   "hold; and, each workgroup streaming one contiguous range, a 16-byte copy, "
                    "16-byte writes, and three 16-byte reads per 16-byte write (the causal walk's mix), each the "
                    "best of plain and non-temporal loads and stores at 512 and 2048 workgroups; and the same 3:1 "
                    "mix in the causal walk's structure (1024 one-wave workgroups, four per CU, one 24 KB chunk "
