@@ -180,6 +180,49 @@ def stream_probes(torch) -> dict:
     return res
 
 
+def two_stream_forward(la, torch, w) -> dict:
+    """The headline forward as one call against its two batch halves on two
+    streams (default priority): whether one half's read-only totals pass can
+    overlap the other half's walk and raise the bytes moved per second."""
+    from workloads import forward_inputs
+    assert w.B == 2
+    q, k, v = (t.cuda() for t in forward_inputs(w))
+    halves = [(q[i:i + 1], k[i:i + 1], v[i:i + 1]) for i in range(2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    main = torch.cuda.current_stream()
+
+    def one():
+        la.forward(q, k, v, causal=True)
+
+    def two():
+        for s in streams:
+            s.wait_stream(main)
+        for s, (a, b, c) in zip(streams, halves):
+            with torch.cuda.stream(s):
+                la.forward(a, b, c, causal=True)
+        for s in streams:
+            main.wait_stream(s)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(15):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        return sorted(times)[len(times) // 2]
+
+    res = {"one_call_ms": timed(one), "two_streams_ms": timed(two),
+           "what": f"{w.name} as one call, and as its two batch halves on two streams (median of 15)"}
+    del q, k, v, halves
+    return res
+
+
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -770,6 +813,8 @@ def main():
         # The walk moves three reads to one write: its rate against the probe
         # of that mix measured now, on this device.
         result["roofline"]["frac_of_probe_mix31"] = achieved / probes["mix_3_reads_1_write"]["GBs"]
+        log("two-stream forward")
+        probes["two_stream_forward"] = two_stream_forward(la, torch, w)
     if not args.no_noncausal:
         for key, name in (("causal_cifar_shaped", "causal_bf16_b16h8n3072"), ("noncausal", "noncausal_bf16_b8h8n4096")):
             wn = WORKLOADS[name]
