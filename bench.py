@@ -180,46 +180,51 @@ def stream_probes(torch) -> dict:
     return res
 
 
-def two_stream_forward(la, torch, w) -> dict:
+def two_stream_forward(la, torch, w, reps: int = 20) -> dict:
     """The headline forward as one call against its two batch halves on two
-    streams (default priority): whether one half's read-only totals pass can
-    overlap the other half's walk and raise the bytes moved per second."""
+    streams (default priority), each timed over `reps` calls (or pairs) issued
+    back to back with preallocated outputs and workspaces: whether one half's
+    read-only totals pass can overlap the other half's walk and raise the
+    bytes moved per second."""
     from workloads import forward_inputs
     assert w.B == 2
     q, k, v = (t.cuda() for t in forward_inputs(w))
-    halves = [(q[i:i + 1], k[i:i + 1], v[i:i + 1]) for i in range(2)]
+    o = torch.empty_like(v)
+    ws = torch.empty(la.workspace_bytes(w.B, w.H, w.N, q.dtype, True), dtype=torch.uint8, device="cuda")
+    halves = []
+    for i in range(2):
+        hws = torch.empty(la.workspace_bytes(1, w.H, w.N, q.dtype, True), dtype=torch.uint8, device="cuda")
+        halves.append((q[i:i + 1], k[i:i + 1], v[i:i + 1], o[i:i + 1], hws))
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     main = torch.cuda.current_stream()
 
     def one():
-        la.forward(q, k, v, causal=True)
+        la.forward(q, k, v, causal=True, out=o, workspace=ws)
 
     def two():
+        for s, (a, b, c, out, hws) in zip(streams, halves):
+            la.forward(a, b, c, causal=True, out=out, workspace=hws, stream=s)
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main)
         for s in streams:
             s.wait_stream(main)
-        for s, (a, b, c) in zip(streams, halves):
-            with torch.cuda.stream(s):
-                la.forward(a, b, c, causal=True)
+        for _ in range(n):
+            fn()
         for s in streams:
             main.wait_stream(s)
-
-    def timed(fn):
-        for _ in range(3):
-            fn()
+        e1.record(main)
         torch.cuda.synchronize()
-        times = []
-        for _ in range(15):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            torch.cuda.synchronize()
-            times.append(a.elapsed_time(b))
-        return sorted(times)[len(times) // 2]
+        return e0.elapsed_time(e1) / n
 
-    res = {"one_call_ms": timed(one), "two_streams_ms": timed(two),
-           "what": f"{w.name} as one call, and as its two batch halves on two streams (median of 15)"}
-    del q, k, v, halves
+    timed(one, 3)
+    timed(two, 3)
+    res = {"one_call_ms": timed(one, reps), "two_streams_ms_per_pair": timed(two, reps),
+           "what": f"{w.name} as one call, and as its two batch halves on two streams; {reps} calls (pairs) "
+                   "back to back, ms per call (pair)"}
+    del q, k, v, o, ws, halves
     return res
 
 
