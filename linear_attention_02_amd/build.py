@@ -1,6 +1,6 @@
 """Builds liblinattn.so (HIP, gfx950) in-tree.
 
-    python -m linear_attention_02_amd.build [-v] [--walk-tiles 2 [--walk-ring] --out PATH]
+    python -m linear_attention_02_amd.build [-v] [--walk-tiles 2 [--walk-ring]] [--scan-grouped-from N] [--out PATH]
 
 Also builds ``validate_host`` objects with the host compiler only when asked
 (``--host-check``), for sanitizer runs of the argument checks without HIP.
@@ -35,11 +35,13 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False, extra=None, walk_tiles: int = 0, walk_ring: bool = False, out: str = None) -> str:
+def build(verbose: bool = False, extra=None, walk_tiles: int = 0, walk_ring: bool = False, out: str = None,
+          scan_grouped_from: int = 0) -> str:
     """Compiles liblinattn.so (or ``out``).  walk_tiles = 2 builds the bf16
     causal walk with 32-token chunks instead of 64 (a measurement variant);
     walk_ring adds a three-slot LDS ring with two chunks in flight, one wave
-    per SIMD (with walk_tiles = 2)."""
+    per SIMD (with walk_tiles = 2); scan_grouped_from = N sends N records per
+    head or more to the grouped scan instead of 128 (a measurement variant)."""
     lib = out or LIB
     tmp = lib + ".tmp"
     obj_dir = os.path.join(HERE, "_build" if not out else "_build_" + os.path.basename(out).replace(".", "_"))
@@ -48,6 +50,8 @@ def build(verbose: bool = False, extra=None, walk_tiles: int = 0, walk_ring: boo
         extra.append(f"-DLINATTN_WALK_TILES_BF16={int(walk_tiles)}")
     if walk_ring:
         extra.append("-DLINATTN_WALK_RING=1")
+    if scan_grouped_from:
+        extra.append(f"-DLINATTN_SCAN_GROUPED_FROM={int(scan_grouped_from)}")
     os.makedirs(obj_dir, exist_ok=True)
     api_o = os.path.join(obj_dir, "api.o")
     val_o = os.path.join(obj_dir, "validate.o")
@@ -100,7 +104,9 @@ if __name__ == "__main__":
                     help="row tiles per chunk of the bf16 causal walk (2: 32-token chunks; default 4)")
     ap.add_argument("--walk-ring", action="store_true",
                     help="with --walk-tiles 2: three-slot ring, two chunks in flight, one wave per SIMD")
+    ap.add_argument("--scan-grouped-from", type=int, default=0,
+                    help="records per head from which the grouped scan runs (default 128)")
     ap.add_argument("--out", default=None, help="output path (default: linear_attention_02_amd/liblinattn.so)")
     args, rest = ap.parse_known_args()
     build(verbose=args.v, extra=[a for a in rest if a.startswith("-R")], walk_tiles=args.walk_tiles,
-          walk_ring=args.walk_ring, out=args.out)
+          walk_ring=args.walk_ring, out=args.out, scan_grouped_from=args.scan_grouped_from)

@@ -120,8 +120,14 @@ template <class E> TotalsKernel<E> totals_kernel(long long heads, long long N) {
 
 // One thread per (head, W state elements): W = 4 while that still launches
 // 256 blocks or more, else 1; a batch of eight loads for up to eight records.
-// More than kScanGroupedFrom records per head go to the grouped scan instead.
-constexpr int kScanGroupedFrom = 128;
+// kScanGroupedFrom records per head or more go to the grouped scan instead
+// (128; a measurement build may set LINATTN_SCAN_GROUPED_FROM lower to compare
+// the two forms on fewer records).
+#ifndef LINATTN_SCAN_GROUPED_FROM
+#define LINATTN_SCAN_GROUPED_FROM 128
+#endif
+constexpr int kScanGroupedFrom = LINATTN_SCAN_GROUPED_FROM;
+static_assert(kScanGroupedFrom >= 1, "grouped scan threshold");
 
 void launch_scan(const FwdParams &p, int mode, hipStream_t stream) {
   const int cnt = mode == kScanTotal ? p.segments : p.segments - 1;
