@@ -1321,10 +1321,13 @@ __global__ __launch_bounds__(64 * kGroupWaves, 1) void noncausal_read_kernel(Fwd
       } else {
         wait_vmcnt<8>();
       }
+      // Untracked reads: a compiler-visible LDS read here would also wait for
+      // the previous chunk's output stores, a full store round trip per chunk.
       Frag<E> qf[4][4];
 #pragma unroll
-      for (int it = 0; it < 4; ++it) lds_row_frags(slot, 0, it, lane, qf[it]);
-      wait_lgkmcnt0();
+      for (int it = 0; it < 4; ++it) lds_row_frags_untracked(slot, 0, it, lane, qf[it]);
+      lds_reads_done();  // the slot is refilled only after every lane's read of it returned
+      after_lds_reads<16>(&qf[0][0]);
       if (t0 + kChunk < t_end) stage_issue<1>(slot, src, t0 + kChunk, chunk_rows(t0 + kChunk, t_end), n16, g);
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
